@@ -1,0 +1,95 @@
+// Combine: weighted sum of a token's expert outputs, written at the token's
+// original position.
+//
+// At the source the results of the selected experts are summed with the
+// combine weights, e.g. y(A2) = 0.7 u0 + 0.3 u2 ("EP: Partition Experts and
+// Route Tokens", "Return multiple expert results to the same token"), and the
+// outputs return in input order. A token whose experts all live on other
+// ranks gets zeros, so the ranks' outputs add up to the full layer ("Expert
+// Parallelism (EP)", "Why a Single All-Reduce/Reduce-Scatter Works").
+//
+// One wave per token; the sum runs in float32 over the slots in order and is
+// rounded to bf16 once.
+#include "gemm_tile.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+template <int KMAX>
+__global__ void __launch_bounds__(kThreads)
+combine_kernel(const uint16_t* __restrict__ expert_out, const int32_t* __restrict__ inv,
+               const float* __restrict__ topk_w, int T, int H, int k, uint16_t* __restrict__ y) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = lane_id();
+  const int d = lane < k ? inv[int64_t(t) * k + lane] : -1;
+  const float wl = lane < k ? topk_w[int64_t(t) * k + lane] : 0.f;
+  const uint64_t dests = ballot(d >= 0);
+  // Local slots in slot order, broadcast to every lane.
+  int rows[KMAX];
+  float wts[KMAX];
+  int nl = 0;
+  {
+    uint64_t mm = dests;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      rows[j] = 0;
+      wts[j] = 0.f;
+      if (mm) {
+        const int s = __ffsll((unsigned long long)mm) - 1;
+        mm &= mm - 1;
+        rows[j] = shfl(d, s);
+        wts[j] = shfl(wl, s);
+        ++nl;
+      }
+    }
+  }
+  // Start from -0 so that a single term passes through bit for bit (-0 + -0 = -0);
+  // a token with no local slot is written as +0.
+  const float init = nl > 0 ? -0.f : 0.f;
+  const int nv = H / 8;
+  u32x4* dst = reinterpret_cast<u32x4*>(y + int64_t(t) * H);
+  for (int v = lane; v < nv; v += 64) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = init;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j < nl) {
+        const u32x4 q = reinterpret_cast<const u32x4*>(expert_out + int64_t(rows[j]) * H)[v];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = fmaf(wts[j], bf16_lo(q[i]), acc[2 * i]);
+          acc[2 * i + 1] = fmaf(wts[j], bf16_hi(q[i]), acc[2 * i + 1]);
+        }
+      }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+    dst[v] = o;
+  }
+}
+
+hipError_t launch_combine(const uint16_t* expert_out, const int32_t* inv, const float* topk_w, int T, int H, int k,
+                          uint16_t* y, hipStream_t stream) {
+  const dim3 grid(unsigned(ceil_div(T, 4)));
+#define MOE_COMBINE_LAUNCH(KM) \
+  hipLaunchKernelGGL(combine_kernel<KM>, grid, dim3(kThreads), 0, stream, expert_out, inv, topk_w, T, H, k, y)
+  if (k <= 1)
+    MOE_COMBINE_LAUNCH(1);
+  else if (k <= 2)
+    MOE_COMBINE_LAUNCH(2);
+  else if (k <= 4)
+    MOE_COMBINE_LAUNCH(4);
+  else if (k <= 8)
+    MOE_COMBINE_LAUNCH(8);
+  else if (k <= 16)
+    MOE_COMBINE_LAUNCH(16);
+  else
+    MOE_COMBINE_LAUNCH(32);
+#undef MOE_COMBINE_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,207 @@
+// Dispatch: group the rank's (token, slot) selections by expert.
+//
+// Token vectors, not weights and not router scores, move to the selected
+// experts, and each expert's rows are stacked so one matmul serves them
+// ("EP: Partition Experts and Route Tokens", section "Send tokens to experts
+// and return their results"); counting every expert's selections gives the
+// per-expert load that "Equal expert counts can receive different token
+// counts" is about. The rank keeps only its contiguous expert block
+// [e0, e0 + E_local) ("Expert Parallelism (EP)", "Limitations").
+//
+// Row order is deterministic: segment of expert e0+i first by i, inside a
+// segment by token. Four kernels, no host synchronisation:
+//   1. histogram: one wave per chunk of 64 tokens counts its selections of
+//      every expert with LDS atomics -> chunk_table[e][chunk];
+//   2. scan: one workgroup per expert turns its row of chunk_table into
+//      exclusive prefixes and writes counts[e];
+//   3. index: one wave per chunk gives every local selection its row
+//      (segment start + chunk prefix + rank among earlier lanes that picked
+//      the same expert, found with one ballot per distinct expert) and fills
+//      perm_src and inv;
+//   4. copy: one wave per token reads the token vector once and writes it to
+//      each of its rows.
+#include "gemm_tile.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+__global__ void __launch_bounds__(kThreads)
+dispatch_hist_kernel(const int32_t* __restrict__ topk_idx, int T, int E, int k, int nchunks,
+                     int32_t* __restrict__ chunk_table) {
+  extern __shared__ int s_hist[];  // 4 waves x E
+  const int w = threadIdx.x >> 6;
+  const int lane = lane_id();
+  int* hist = s_hist + w * E;
+  for (int e = lane; e < E; e += 64) hist[e] = 0;
+  __syncthreads();
+  const int c = blockIdx.x * 4 + w;
+  const int t = c * kChunk + lane;
+  if (c < nchunks && t < T) {
+    const int32_t* sel = topk_idx + int64_t(t) * k;
+    for (int j = 0; j < k; ++j) atomicAdd(&hist[sel[j]], 1);
+  }
+  __syncthreads();
+  if (c < nchunks)
+    for (int e = lane; e < E; e += 64) chunk_table[int64_t(e) * nchunks + c] = hist[e];
+}
+
+__global__ void __launch_bounds__(kThreads)
+dispatch_scan_kernel(int32_t* __restrict__ chunk_table, int nchunks, int32_t* __restrict__ counts) {
+  __shared__ int s_tmp[4];
+  const int e = blockIdx.x;
+  int32_t* row = chunk_table + int64_t(e) * nchunks;
+  int carry = 0;
+  for (int base = 0; base < nchunks; base += kThreads) {
+    const int i = base + threadIdx.x;
+    const int v = i < nchunks ? row[i] : 0;
+    int tot;
+    const int pre = block_exclusive_scan(v, s_tmp, tot);
+    if (i < nchunks) row[i] = carry + pre;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) counts[e] = carry;
+}
+
+template <int KMAX>
+__global__ void __launch_bounds__(kThreads)
+dispatch_index_kernel(const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ chunk_base,
+                      const int32_t* __restrict__ counts, int T, int k, int e0, int E_local, int nchunks,
+                      int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src, int32_t* __restrict__ inv) {
+  __shared__ int s_seg[1024 + 1];
+  __shared__ int s_tmp[4];
+  // Segment starts: exclusive scan of the local experts' counts (4 per thread).
+  int cnt[4];
+  int sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = threadIdx.x * 4 + q;
+    cnt[q] = i < E_local ? counts[e0 + i] : 0;
+    sum += cnt[q];
+  }
+  int tot;
+  int pre = block_exclusive_scan(sum, s_tmp, tot);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = threadIdx.x * 4 + q;
+    if (i < E_local) s_seg[i] = pre;
+    pre += cnt[q];
+  }
+  if (threadIdx.x == 0) s_seg[E_local] = tot;
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= E_local; i += kThreads) offsets[i] = s_seg[i];
+
+  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (c >= nchunks) return;
+  const int lane = lane_id();
+  const int t = c * kChunk + lane;
+  const bool valid = t < T;
+  int ev[KMAX];
+  uint32_t pend = 0;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    ev[j] = -1;
+    if (j < k && valid) {
+      const int e = topk_idx[int64_t(t) * k + j];
+      ev[j] = e;
+      if (e >= e0 && e < e0 + E_local)
+        pend |= 1u << j;
+      else
+        inv[int64_t(t) * k + j] = -1;
+    }
+  }
+  while (true) {
+    const uint64_t active = ballot(pend != 0);
+    if (active == 0) break;
+    const int leader = __ffsll((unsigned long long)active) - 1;
+    int first = -1;
+#pragma unroll
+    for (int j = KMAX - 1; j >= 0; --j)
+      if ((pend >> j) & 1u) first = ev[j];
+    const int e_lead = shfl(first, leader);
+    int js = -1;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (((pend >> j) & 1u) && ev[j] == e_lead) js = j;
+    const uint64_t mask = ballot(js >= 0);
+    if (js >= 0) {
+      const int rank = __popcll(mask & lanemask_lt());
+      const int row = s_seg[e_lead - e0] + chunk_base[int64_t(e_lead) * nchunks + c] + rank;
+      const int64_t slot = int64_t(t) * k + js;
+      perm_src[row] = int32_t(slot);
+      inv[slot] = row;
+      pend &= ~(1u << js);
+    }
+  }
+}
+
+// One wave per token; U 16-byte chunks in flight per lane.
+__global__ void __launch_bounds__(kThreads)
+dispatch_copy_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ inv, int T, int H, int k,
+                     uint16_t* __restrict__ x_perm) {
+  constexpr int U = 4;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = lane_id();
+  const int d = lane < k ? inv[int64_t(t) * k + lane] : -1;
+  const uint64_t dests = ballot(d >= 0);
+  if (dests == 0) return;
+  const int nv = H / 8;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + int64_t(t) * H);
+  for (int v0 = 0; v0 < nv; v0 += 64 * U) {
+    u32x4 q[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = v0 + u * 64 + lane;
+      if (v < nv) q[u] = src[v];
+    }
+    uint64_t mm = dests;
+    while (mm) {
+      const int j = __ffsll((unsigned long long)mm) - 1;
+      mm &= mm - 1;
+      const int row = shfl(d, j);
+      u32x4* dst = reinterpret_cast<u32x4*>(x_perm + int64_t(row) * H);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * 64 + lane;
+        if (v < nv) dst[v] = q[u];
+      }
+    }
+  }
+}
+
+hipError_t launch_dispatch(const uint16_t* x, const int32_t* topk_idx, int T, int H, int E, int k, int e0,
+                           int E_local, int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv,
+                           uint16_t* x_perm, int32_t* chunk_table, hipStream_t stream) {
+  const int nchunks = int(ceil_div(T, kChunk));
+  const unsigned wgs = unsigned(ceil_div(nchunks, 4));
+  hipLaunchKernelGGL(dispatch_hist_kernel, dim3(wgs), dim3(kThreads), size_t(4) * E * sizeof(int), stream,
+                     topk_idx, T, E, k, nchunks, chunk_table);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(unsigned(E)), dim3(kThreads), 0, stream, chunk_table, nchunks,
+                     counts);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+#define MOE_INDEX_LAUNCH(KM)                                                                                  \
+  hipLaunchKernelGGL(dispatch_index_kernel<KM>, dim3(wgs), dim3(kThreads), 0, stream, topk_idx, chunk_table, \
+                     counts, T, k, e0, E_local, nchunks, offsets, perm_src, inv)
+  if (k <= 1)
+    MOE_INDEX_LAUNCH(1);
+  else if (k <= 2)
+    MOE_INDEX_LAUNCH(2);
+  else if (k <= 4)
+    MOE_INDEX_LAUNCH(4);
+  else if (k <= 8)
+    MOE_INDEX_LAUNCH(8);
+  else if (k <= 16)
+    MOE_INDEX_LAUNCH(16);
+  else
+    MOE_INDEX_LAUNCH(32);
+#undef MOE_INDEX_LAUNCH
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(dispatch_copy_kernel, dim3(unsigned(ceil_div(T, 4))), dim3(kThreads), 0, stream, x, inv, T,
+                     H, k, x_perm);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,187 @@
+// Expert MLPs as grouped GEMMs over ragged expert segments.
+//
+// Each local expert i owns gate_up [H, 2I] (gate = columns [0, I), up =
+// columns [I, 2I)) and down [I, H] ("Expert Parallelism (EP)", AWS Neuron
+// vLLM design doc, weight-shape table under "Expert Weight Distribution").
+// Its rows are the dispatched segment [offsets[i], offsets[i+1]), stacked into
+// one matmul because every token is transformed on its own ("EP: Partition
+// Experts and Route Tokens", "Send tokens to experts and return their
+// results"). Segment lengths are data dependent and read on the device, so no
+// host synchronisation sits between dispatch and the GEMMs.
+//
+//   GEMM1:  h   = silu(X Wg) * (X Wu)   fused: one tile computes matching
+//                                      gate and up columns and writes h
+//   GEMM2:  out = h Wd
+//
+// Both are persistent kernels: every workgroup rebuilds the tile list from
+// `offsets` (m-tiles of BM rows per segment x n-tiles) and strides over it.
+// Weights are n-contiguous in memory and are transposed 8 x 8 in registers on
+// their way to LDS, so both MFMA operands are read k-contiguous from LDS.
+#include "gemm_tile.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+constexpr int kMaxLocal = 1024;
+
+template <int BM, bool SWIGLU>
+__global__ void __launch_bounds__(kThreads)
+grouped_gemm_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __restrict__ offsets, int E_local,
+                    int64_t capacity, const uint16_t* __restrict__ W, int64_t w_expert_stride, int ldw,
+                    uint16_t* __restrict__ C, int ldc, int K, int N, int up_off) {
+  constexpr int BN = 256;
+  constexpr int FM = BM / 64;
+  constexpr int FN = 4;
+  __shared__ __attribute__((aligned(16))) uint16_t As[BM * kLdk];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * kLdk];
+  __shared__ int s_off[kMaxLocal + 1];
+  __shared__ int s_tpre[kMaxLocal + 1];
+  __shared__ int s_tmp[4];
+
+  // Segment bounds (clamped into [0, capacity]) and the m-tile prefix.
+  int mt[4];
+  int sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = threadIdx.x * 4 + q;
+    mt[q] = 0;
+    if (i < E_local) {
+      const int64_t a = min<int64_t>(max<int64_t>(offsets[i], 0), capacity);
+      const int64_t b = max<int64_t>(a, min<int64_t>(offsets[i + 1], capacity));
+      s_off[i] = int(a);
+      mt[q] = int((b - a + BM - 1) / BM);
+      if (i == E_local - 1) s_off[E_local] = int(b);
+    }
+    sum += mt[q];
+  }
+  int total_mt;
+  int pre = block_exclusive_scan(sum, s_tmp, total_mt);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = threadIdx.x * 4 + q;
+    if (i < E_local) s_tpre[i] = pre;
+    pre += mt[q];
+  }
+  __syncthreads();
+
+  const int ntn = SWIGLU ? (N + 127) / 128 : (N + 255) / 256;
+  const int total = total_mt * ntn;
+  const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int lane = lane_id();
+  const int nk = (K + kBK - 1) / kBK;
+
+  for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int gm = tile / ntn;
+    const int nj = tile - gm * ntn;
+    int lo = 0, hi = E_local - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_tpre[mid] <= gm)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const int e = lo;
+    const int r0 = s_off[e] + (gm - s_tpre[e]) * BM;
+    const int rows = min(BM, s_off[e + 1] - r0);
+    const uint16_t* We = W + int64_t(e) * w_expert_stride;
+
+    auto row_ptr = [&](int r) { return A + int64_t(r0 + min(r, rows - 1)) * lda; };
+    auto col_of = [&](int s0) -> int {
+      if (SWIGLU) {
+        const int q = s0 & 127;
+        const int oc = nj * 128 + (s0 >> 7) * 64 + (q & 63);
+        if (oc >= N) return -1;
+        return q < 64 ? oc : up_off + oc;
+      } else {
+        const int oc = nj * 256 + s0;
+        return oc < N ? oc : -1;
+      }
+    };
+
+    f32x16 acc[FM][FN];
+    zero_acc(acc);
+    KRowsLoader<BM> la;
+    NColsTransposeLoader lb;
+    la.load(row_ptr, 0, K);
+    lb.load(We, ldw, col_of, 0, K);
+    for (int kt = 0; kt < nk; ++kt) {
+      __syncthreads();
+      la.store(As);
+      lb.store(Bs);
+      __syncthreads();
+      if (kt + 1 < nk) {
+        la.load(row_ptr, (kt + 1) * kBK, K);
+        lb.load(We, ldw, col_of, (kt + 1) * kBK, K);
+      }
+      mma_stage<FM, FN, 1, BN>(As, Bs, wm * (BM / 2), wn * 128, acc);
+    }
+
+    if (SWIGLU) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn) {
+          const int col = nj * 128 + wn * 64 + fn * 32 + (lane & 31);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = wm * (BM / 2) + fm * 32 + mfma_c_row(v, lane);
+            if (row < rows && col < N) {
+              const float g = acc[fm][fn][v];
+              const float u = acc[fm][fn + 2][v];
+              const float hv = g / (1.f + __expf(-g)) * u;
+              C[int64_t(r0 + row) * ldc + col] = uint16_t(f32_to_bf16_bits(hv));
+            }
+          }
+        }
+    } else {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const int col = nj * 256 + wn * 128 + fn * 32 + (lane & 31);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = wm * (BM / 2) + fm * 32 + mfma_c_row(v, lane);
+            if (row < rows && col < N)
+              C[int64_t(r0 + row) * ldc + col] = uint16_t(f32_to_bf16_bits(acc[fm][fn][v]));
+          }
+        }
+    }
+  }
+}
+
+namespace {
+constexpr int kFfnBM = 128;
+unsigned persistent_grid(int64_t tiles) {
+  return unsigned(std::max<int64_t>(1, std::min<int64_t>(tiles, int64_t(device_cu_count()))));
+}
+}  // namespace
+
+hipError_t launch_expert_gemm1(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_gate_up, int H,
+                               int I, int E_local, int64_t capacity, uint16_t* h, hipStream_t stream) {
+  const int64_t mt_bound = ceil_div(capacity, kFfnBM) + E_local;
+  const unsigned grid = persistent_grid(mt_bound * ceil_div(I, 128));
+  hipLaunchKernelGGL((grouped_gemm_kernel<kFfnBM, true>), dim3(grid), dim3(kThreads), 0, stream, x_perm, H, offsets,
+                     E_local, capacity, w_gate_up, int64_t(H) * 2 * I, 2 * I, h, I, H, I, I);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_gemm2(const uint16_t* h, const int32_t* offsets, const uint16_t* w_down, int H, int I,
+                               int E_local, int64_t capacity, uint16_t* out, hipStream_t stream) {
+  const int64_t mt_bound = ceil_div(capacity, kFfnBM) + E_local;
+  const unsigned grid = persistent_grid(mt_bound * ceil_div(H, 256));
+  hipLaunchKernelGGL((grouped_gemm_kernel<kFfnBM, false>), dim3(grid), dim3(kThreads), 0, stream, h, I, offsets,
+                     E_local, capacity, w_down, int64_t(I) * H, H, out, H, I, H, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_ffn(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_gate_up,
+                             const uint16_t* w_down, int H, int I, int E_local, int64_t capacity, uint16_t* h,
+                             uint16_t* out, hipStream_t stream) {
+  hipError_t err = launch_expert_gemm1(x_perm, offsets, w_gate_up, H, I, E_local, capacity, h, stream);
+  if (err != hipSuccess) return err;
+  return launch_expert_gemm2(h, offsets, w_down, H, I, E_local, capacity, out, stream);
+}
+
+}  // namespace moe

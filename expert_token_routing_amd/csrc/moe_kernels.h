@@ -1,0 +1,44 @@
+// Host-side launchers of the MoE kernels (internal; the public C-ABI is moe.h).
+// Every launcher only enqueues on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace moe {
+
+constexpr int kChunk = 64;  // tokens per dispatch chunk (one wave)
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Router: planes must hold 3*E*H bf16.
+hipError_t launch_route(const uint16_t* x, const float* w_router, const float* bias, int T, int H, int E, int k,
+                        int renormalize, float* logits, int32_t* topk_idx, float* topk_w, uint16_t* planes,
+                        hipStream_t stream);
+
+// Dispatch: chunk_table must hold E * ceil(T/64) int32.
+hipError_t launch_dispatch(const uint16_t* x, const int32_t* topk_idx, int T, int H, int E, int k, int e0,
+                           int E_local, int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv,
+                           uint16_t* x_perm, int32_t* chunk_table, hipStream_t stream);
+
+// Grouped SwiGLU expert MLPs over the segments given by device `offsets`.
+hipError_t launch_expert_ffn(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_gate_up,
+                             const uint16_t* w_down, int H, int I, int E_local, int64_t capacity, uint16_t* h,
+                             uint16_t* out, hipStream_t stream);
+
+// The two grouped GEMMs on their own (what launch_expert_ffn runs in order).
+hipError_t launch_expert_gemm1(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_gate_up, int H,
+                               int I, int E_local, int64_t capacity, uint16_t* h, hipStream_t stream);
+hipError_t launch_expert_gemm2(const uint16_t* h, const int32_t* offsets, const uint16_t* w_down, int H, int I,
+                               int E_local, int64_t capacity, uint16_t* out, hipStream_t stream);
+
+// Weighted top-k sum in token order.
+hipError_t launch_combine(const uint16_t* expert_out, const int32_t* inv, const float* topk_w, int T, int H, int k,
+                          uint16_t* y, hipStream_t stream);
+
+// Cached device facts of the current device.
+int device_cu_count();
+
+}  // namespace moe

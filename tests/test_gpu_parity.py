@@ -1,0 +1,374 @@
+"""HIP path against the CPU oracle, through the C-ABI, on one GPU.
+
+Bar (from the problem statement): routing indices, counts, offsets,
+permutations and dispatched rows bit-exact given identical router logits;
+expert outputs and the combined output within max relative error 2e-2
+(bf16 inputs, float32 accumulation). Small sizes are compared element by
+element; the full-size workloads on sampled rows that the oracle computes one
+by one, plus properties that hold at any size.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import expert_token_routing_amd as M
+import oracle.moe_oracle as O
+import workloads as W
+from tests import oracle_pins as P
+from tests.gpu_helpers import (OUT_TOL, W_RTOL, DevInputs, bf16_bits, bf16_f64, device, rel_max_err, say,
+                               to_dev, to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+_INPUT_CACHE: dict = {}
+
+
+def inputs_for(cfg: W.MoEConfig) -> W.MoEInputs:
+    key = cfg
+    if key not in _INPUT_CACHE:
+        _INPUT_CACHE.clear()
+        _INPUT_CACHE[key] = W.make_inputs(cfg)
+    return _INPUT_CACHE[key]
+
+
+def ragged(name, **kw):
+    return W.MoEConfig(name, **kw)
+
+
+# Small problems the oracle finishes in seconds; they span several tiles in
+# every kernel and end in ragged tails (T not a multiple of 64/128, H and I
+# not multiples of the 64-wide k stage or the 128/256-wide n tiles).
+SMALL_CASES = [
+    W.CONFIGS["tiny_top1"],
+    ragged("ragged_a", T=300, H=200, I=136, E=12, k=3, e0=4, E_local=5),
+    ragged("ragged_b", T=517, H=264, I=392, E=40, k=6, e0=0, E_local=40, renormalize=0),
+    ragged("ragged_c", T=129, H=72, I=24, E=7, k=7, e0=6, E_local=1),
+    ragged("single_token", T=1, H=64, I=64, E=9, k=2, e0=0, E_local=9),
+    ragged("many_experts", T=257, H=136, I=72, E=1024, k=32, e0=512, E_local=96),
+]
+
+
+# --------------------------------------------------------------------------- #
+# step-by-step runner                                                          #
+# --------------------------------------------------------------------------- #
+def run_steps(d: DevInputs):
+    cfg = d.cfg
+    say(f"moe_route {cfg.name} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k}")
+    logits, idx, w = M.moe_route(d.x, d.w_router, d.bias, cfg.k, cfg.renormalize)
+    torch.cuda.synchronize()
+    say(f"moe_dispatch {cfg.name} e0={cfg.e0} E_local={cfg.E_local}")
+    counts, offsets, perm_src, inv, x_perm = M.moe_dispatch(d.x, idx, cfg.E, cfg.e0, cfg.E_local)
+    torch.cuda.synchronize()
+    res = dict(logits=logits, idx=idx, w=w, counts=counts, offsets=offsets, perm_src=perm_src, inv=inv,
+               x_perm=x_perm)
+    if d.w_gate_up is not None:
+        say(f"moe_expert_ffn {cfg.name} I={cfg.I}")
+        h, out = M.moe_expert_ffn(x_perm, offsets, d.w_gate_up, d.w_down)
+        torch.cuda.synchronize()
+        say(f"moe_combine {cfg.name}")
+        y = M.moe_combine(out, inv, w)
+        torch.cuda.synchronize()
+        res.update(h=h, out=out, y=y)
+    return res
+
+
+def check_route(cfg, inp, logits, idx, w):
+    """Logits within float32 accuracy of the float64 definition; selection
+    and weights exactly / tightly equal to the oracle's on the same logits."""
+    gl = logits.cpu().numpy().astype(np.float64)
+    ref = O.oracle_logits(inp.x, inp.w_router, inp.bias)
+    xa = np.abs(O.bf16_to_f64(inp.x))
+    bound = 1e-5 * (xa @ np.abs(inp.w_router.astype(np.float64)).T) + 1e-6
+    assert np.all(np.abs(gl - ref) <= bound), float(np.max(np.abs(gl - ref) / bound))
+    gi = idx.cpu().numpy()
+    ri = O.oracle_topk(gl, cfg.k)
+    assert np.array_equal(gi, ri), np.argwhere(gi != ri)[:5]
+    rw = O.oracle_weights(gl, ri, cfg.renormalize)
+    gw = w.cpu().numpy().astype(np.float64)
+    assert np.allclose(gw, rw, rtol=W_RTOL, atol=1e-7), float(np.max(np.abs(gw - rw)))
+    # where the float64 logits leave a clear margin, their selection agrees too
+    srt = -np.sort(-ref, axis=1)
+    if cfg.k < cfg.E:
+        margin = srt[:, cfg.k - 1] - srt[:, cfg.k]
+        clear = margin > 1e-3
+        r64 = O.oracle_topk(ref, cfg.k)
+        assert np.array_equal(np.sort(gi[clear], 1), np.sort(r64[clear], 1))
+    return gl, gi, gw
+
+
+def check_dispatch(cfg, inp, gi, res):
+    counts, offsets, perm_src, inv = (res[n].cpu().numpy() for n in ("counts", "offsets", "perm_src", "inv"))
+    rc = O.oracle_counts(gi, cfg.E)
+    ro = O.oracle_offsets(rc, cfg.e0, cfg.E_local)
+    rp, rinv = O.oracle_permutation(gi, cfg.e0, cfg.E_local)
+    assert np.array_equal(counts, rc)
+    assert int(counts.sum()) == cfg.T * cfg.k
+    assert np.array_equal(offsets, ro)
+    N = int(ro[-1])
+    assert np.array_equal(perm_src[:N], rp)
+    assert np.array_equal(inv, rinv)
+    # x_perm rows are the token vectors, bit for bit (property check on the GPU)
+    src = torch.from_numpy(rp.astype(np.int64) // cfg.k).to(res["x_perm"].device)
+    xs = res["x_perm"][:N].view(torch.int16)
+    ok = torch.equal(xs, to_dev_bf16(inp.x, xs.device).view(torch.int16)[src])
+    assert ok, "x_perm differs from x[perm_src // k]"
+    return N, ro, rp, rinv
+
+
+def sample_rows(offsets, per_expert, rng):
+    """Rows to check: the first and last rows of each segment, rows around
+    m-tile boundaries, and a random draw."""
+    rows = []
+    E_local = len(offsets) - 1
+    for i in range(E_local):
+        a, b = int(offsets[i]), int(offsets[i + 1])
+        if b <= a:
+            continue
+        cand = {a, b - 1, min(b - 1, a + 127), min(b - 1, a + 128), min(b - 1, a + 255)}
+        if b - a > per_expert:
+            cand.update(rng.choice(np.arange(a, b), size=per_expert, replace=False).tolist())
+        else:
+            cand.update(range(a, b))
+        rows.extend(sorted(cand))
+    return np.asarray(sorted(set(rows)), dtype=np.int64)
+
+
+def expert_of_rows(offsets, rows):
+    return np.searchsorted(np.asarray(offsets), rows, side="right") - 1
+
+
+def check_ffn(cfg, inp, res, N, ro, rows=None):
+    out = res["out"]
+    if rows is None:
+        rows = np.arange(N)
+    if rows.size == 0:
+        return
+    ex = expert_of_rows(ro, rows)
+    got = bf16_f64(out[torch.from_numpy(rows).to(out.device)])
+    xp = bf16_bits(res["x_perm"][torch.from_numpy(rows).to(out.device)])
+    ref = np.zeros_like(got)
+    for i in np.unique(ex):
+        sel = ex == i
+        ref[sel] = O.oracle_expert_mlp(xp[sel], inp.w_gate_up[i], inp.w_down[i])
+    err = rel_max_err(got, ref)
+    assert err <= OUT_TOL, err
+
+
+def check_combine(cfg, res, gw, rinv):
+    """y against the oracle's combine of the GPU's own expert outputs."""
+    y = bf16_f64(res["y"])
+    N = int(np.max(rinv)) + 1 if np.any(rinv >= 0) else 0
+    outs = bf16_bits(res["out"][:max(N, 1)])
+    ref = O.oracle_combine(outs, rinv, gw, cfg.T, cfg.k)
+    assert rel_max_err(y, ref) <= OUT_TOL
+    none = ~(rinv.reshape(cfg.T, cfg.k) >= 0).any(1)
+    assert np.all(y[none] == 0.0)
+
+
+# --------------------------------------------------------------------------- #
+# tests                                                                        #
+# --------------------------------------------------------------------------- #
+def test_mfma_router_split_is_exact():
+    """One-hot tokens make each logit a single product x*w = w, so the three
+    bf16 parts must add back to the float32 router weight exactly."""
+    dev = device()
+    rng = np.random.default_rng(5)
+    T, H, E = 192, 136, 70
+    xf = np.zeros((T, H), np.float32)
+    hsel = rng.integers(0, H, size=T)
+    xf[np.arange(T), hsel] = 1.0
+    x = W.bf16_bits_from_f32(xf)
+    wr = (rng.standard_normal((E, H)) * np.exp(rng.uniform(-20, 20, (E, H)))).astype(np.float32)
+    say("moe_route split exactness T=192 H=136 E=70")
+    logits, idx, w = M.moe_route(to_dev_bf16(x, dev), to_dev(wr, dev), None, 3, True)
+    gl = logits.cpu().numpy()
+    assert np.array_equal(gl, wr[:, hsel].T), np.argwhere(gl != wr[:, hsel].T)[:4]
+
+
+@pytest.mark.parametrize("cfg", SMALL_CASES, ids=lambda c: c.name)
+def test_small_case_all_steps(cfg):
+    """Every step, every element, on problems the oracle finishes at once."""
+    dev = device()
+    inp = W.make_inputs(cfg)
+    d = DevInputs(inp, dev)
+    res = run_steps(d)
+    gl, gi, gw = check_route(cfg, inp, res["logits"], res["idx"], res["w"])
+    N, ro, rp, rinv = check_dispatch(cfg, inp, gi, res)
+    check_ffn(cfg, inp, res, N, ro)
+    check_combine(cfg, res, gw, rinv)
+    # end to end against the oracle (routing on the GPU's float32 logits)
+    y_ref = O.oracle_forward(inp.x, inp.w_router, inp.bias, inp.w_gate_up, inp.w_down, cfg.k, cfg.e0,
+                             cfg.E_local, cfg.renormalize, logits=gl)
+    assert rel_max_err(bf16_f64(res["y"]), y_ref) <= OUT_TOL
+    # the fused entry point gives the same bits as the four steps
+    say(f"moe_forward {cfg.name}")
+    y, _ = M.moe_forward(d.x, d.w_router, d.bias, d.w_gate_up, d.w_down, cfg.k, cfg.e0, cfg.renormalize)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), res["y"].view(torch.int16))
+
+
+def test_identity_experts_return_tokens_unchanged():
+    """Tiny top-1 workload with identity experts (combine applied to the
+    dispatched rows): every token comes back bit for bit in its place."""
+    dev = device()
+    cfg = W.CONFIGS["tiny_top1"]
+    inp = W.make_inputs(cfg)
+    d = DevInputs(inp, dev)
+    say("identity round trip tiny_top1")
+    _, idx, w = M.moe_route(d.x, d.w_router, None, 1, True)
+    assert torch.all(w == 1.0)
+    counts, offsets, perm_src, inv, x_perm = M.moe_dispatch(d.x, idx, cfg.E, 0, cfg.E)
+    y = M.moe_combine(x_perm, inv, w)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), d.x.view(torch.int16))
+    assert int(counts.sum()) == cfg.T
+
+
+@pytest.mark.parametrize("fixture", ["walkthrough_top1_4tok.json", "imbalance_top1_8tok.json"])
+def test_pages_dispatch_examples(fixture):
+    """The pages' top-1 walk-through and imbalance example through the GPU
+    router (unit router rows, one-hot tokens) and dispatch, for every share."""
+    dev = device()
+    g = P.load_golden(fixture)
+    want = [r[0] for r in g["topk_idx"]]
+    T, E, H = len(want), g["E"], 64
+    xf = np.zeros((T, H), np.float32)
+    for t in range(T):
+        xf[t, want[t]] = 1.0
+        xf[t, 8:16] = np.arange(8) * 0.25 + t
+    x = to_dev_bf16(W.bf16_bits_from_f32(xf), dev)
+    wr = np.zeros((E, H), np.float32)
+    wr[np.arange(E), np.arange(E)] = 1.0
+    say(f"pages example {fixture}")
+    _, idx, w = M.moe_route(x, to_dev(wr, dev), None, 1, True)
+    assert idx.cpu().numpy().tolist() == g["topk_idx"]
+    for s in g["shares"]:
+        counts, offsets, perm_src, inv, x_perm = M.moe_dispatch(x, idx, E, s["e0"], s["E_local"])
+        torch.cuda.synchronize()
+        assert counts.cpu().tolist() == g["counts"]
+        assert offsets.cpu().tolist() == s["offsets"]
+        n = s["offsets"][-1]
+        assert perm_src[:n].cpu().tolist() == s["perm_src"]
+        assert inv.cpu().tolist() == s["inv"]
+        y = M.moe_combine(x_perm, inv, w)
+        yb = bf16_f64(y)
+        for t in range(T):
+            local = s["e0"] <= want[t] < s["e0"] + s["E_local"]
+            assert np.array_equal(yb[t], xf[t] if local else np.zeros(H))
+
+
+def test_pages_top2_and_top4_shares():
+    """Top-2 (0.7, 0.3) and top-4 ([0.3, 0.25, 0.25, 0.2], tie 7/15) examples:
+    GPU router picks and weights, and each rank share keeps its own terms."""
+    dev = device()
+    for fixture, E, El in [("top2_weighted_sum.json", 4, 2), ("top4_partial_sums.json", 32, 4)]:
+        g = P.load_golden(fixture)
+        k, sel, wts = g["k"], g["selected"], g["weights"]
+        H = 64
+        # logits ln(p) on the selected experts, -20 elsewhere, realised as
+        # x = one-hot(0) * 1 and router column 0 = desired logits
+        lg = np.full(E, -20.0, np.float32)
+        lg[sel] = np.log(np.asarray(wts, np.float32))
+        xf = np.zeros((1, H), np.float32)
+        xf[0, 0] = 1.0
+        wr = np.zeros((E, H), np.float32)
+        wr[:, 0] = lg
+        say(f"pages example {fixture}")
+        _, idx, w = M.moe_route(to_dev_bf16(W.bf16_bits_from_f32(xf), dev), to_dev(wr, dev), None, k, True)
+        assert idx.cpu().numpy().tolist() == [sel]
+        assert np.allclose(w.cpu().numpy()[0], wts, rtol=1e-6, atol=1e-7)
+        # every share's inverse index holds exactly its own selected slots
+        for r in range(E // El):
+            _, _, _, inv, _ = M.moe_dispatch(to_dev_bf16(W.bf16_bits_from_f32(xf), dev), idx, E, r * El, El)
+            loc = [j for j, e in enumerate(sel) if r * El <= e < (r + 1) * El]
+            assert [j for j, v in enumerate(inv.cpu().tolist()) if v >= 0] == loc
+
+
+def test_sum_of_rank_shares_equals_all_local():
+    """Running every rank's share (e0 = r*E_local) and adding the outputs gives
+    the all-local output (the pages' single all-reduce / reduce-scatter)."""
+    dev = device()
+    cfg = W.MoEConfig("shares", T=333, H=128, I=96, E=16, k=4, e0=0, E_local=16)
+    inp = W.make_inputs(cfg)
+    d = DevInputs(inp, dev)
+    say("sum of shares T=333 E=16 k=4")
+    y_all, _ = M.moe_forward(d.x, d.w_router, None, d.w_gate_up, d.w_down, cfg.k, 0)
+    for El in (2, 4, 8):
+        tot = torch.zeros_like(y_all, dtype=torch.float32)
+        for r in range(cfg.E // El):
+            y_r, _ = M.moe_forward(d.x, d.w_router, None, d.w_gate_up[r * El:(r + 1) * El].contiguous(),
+                                   d.w_down[r * El:(r + 1) * El].contiguous(), cfg.k, r * El)
+            tot += y_r.float()
+        torch.cuda.synchronize()
+        assert rel_max_err(tot.cpu().numpy(), bf16_f64(y_all)) <= OUT_TOL
+
+
+def test_deterministic_and_row_independent():
+    """Two runs give identical bits; permuting the tokens permutes the output
+    rows bit for bit (no cross-token mixing, no atomics on the float path)."""
+    dev = device()
+    cfg = W.MoEConfig("perm", T=700, H=256, I=192, E=24, k=5, e0=8, E_local=8)
+    inp = W.make_inputs(cfg)
+    d = DevInputs(inp, dev)
+    say("determinism / permutation T=700")
+    y1, _ = M.moe_forward(d.x, d.w_router, None, d.w_gate_up, d.w_down, cfg.k, cfg.e0)
+    y2, _ = M.moe_forward(d.x, d.w_router, None, d.w_gate_up, d.w_down, cfg.k, cfg.e0)
+    p = torch.from_numpy(np.random.default_rng(3).permutation(cfg.T)).to(dev)
+    yp, _ = M.moe_forward(d.x[p].contiguous(), d.w_router, None, d.w_gate_up, d.w_down, cfg.k, cfg.e0)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(yp.view(torch.int16), y1[p].view(torch.int16))
+
+
+def test_empty_batch_is_noop():
+    dev = device()
+    cfg = W.MoEConfig("empty", T=0, H=64, I=64, E=4, k=2, e0=0, E_local=4)
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=dev)
+    wr = torch.randn(4, 64, device=dev)
+    gu = torch.zeros((4, 64, 128), dtype=torch.bfloat16, device=dev)
+    dn = torch.zeros((4, 64, 64), dtype=torch.bfloat16, device=dev)
+    say("empty batch")
+    y, _ = M.moe_forward(x, wr, None, gu, dn, cfg.k, 0)
+    assert y.shape == (0, 64)
+
+
+# --------------------------------------------------------------------------- #
+# the named workloads at their full sizes                                       #
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("name", ["small_top2", "gptoss20b_ep8_share", "dsr1_ep8_share", "dsr1_ep8_share_zipf"])
+def test_named_workload_full_size(name):
+    cfg = W.CONFIGS[name]
+    dev = device()
+    inp = inputs_for(cfg)
+    d = DevInputs(inp, dev)
+    res = run_steps(d)
+    gl, gi, gw = check_route(cfg, inp, res["logits"], res["idx"], res["w"])
+    N, ro, rp, rinv = check_dispatch(cfg, inp, gi, res)
+    rng = np.random.default_rng(7)
+    rows = np.arange(N) if N <= 4096 else sample_rows(ro, 12, rng)
+    check_ffn(cfg, inp, res, N, ro, rows)
+    check_combine(cfg, res, gw, rinv)
+    say(f"moe_forward {name}")
+    y, _ = M.moe_forward(d.x, d.w_router, d.bias, d.w_gate_up, d.w_down, cfg.k, cfg.e0, cfg.renormalize)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), res["y"].view(torch.int16))
+    # sampled tokens end to end against the oracle's definition
+    toks = rng.choice(cfg.T, size=min(cfg.T, 48), replace=False)
+    yref = np.zeros((toks.size, cfg.H))
+    xs = O.bf16_to_f64(inp.x[toks])
+    for n, t in enumerate(toks):
+        for j in range(cfg.k):
+            e = int(gi[t, j])
+            if cfg.e0 <= e < cfg.e0 + cfg.E_local:
+                i = e - cfg.e0
+                yref[n] += gw[t, j] * O.oracle_expert_mlp(xs[n:n + 1], inp.w_gate_up[i], inp.w_down[i])[0]
+    assert rel_max_err(bf16_f64(y[torch.from_numpy(toks).to(dev)]), yref) <= OUT_TOL
+    if cfg.zipf_s > 0:
+        local = res["counts"].cpu().numpy()[cfg.e0:cfg.e0 + cfg.E_local]
+        mean = cfg.T * cfg.k / cfg.E
+        assert local.max() >= 20 * mean, local.max()
+        assert (local == 0).any()
