@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Throughput of one MI355X's share of an MoE layer (expert parallelism).
+
+A step is one pass of the whole share over one batch of tokens: router
+logits, top-k and combine weights; dispatch (rows grouped by local expert);
+the local experts' SwiGLU MLPs as two grouped GEMMs; combine (weighted top-k
+sum in token order). Default workload: a DeepSeek-R1-shaped layer, rank 0 of
+EP = 8 (T = 16384 tokens, H = 7168, I = 2048, 256 experts of which 32 are
+local, top-8), seeded synthetic inputs resident in HBM before timing.
+
+Prints ONE JSON line on stdout; everything else goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s on 1 GPU; grouped-GEMM % MFMA peak; dispatch/combine % HBM"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak
+STAGES = ["route", "dispatch", "gemm1_gate_up_swiglu", "gemm2_down", "combine"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    import workloads as W
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsr1_ep8_share", choices=list(W.CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048,
+                    help="tokens of the workload the CPU oracle runs on (bounded sample)")
+    ap.add_argument("--cold-steps", type=int, default=5,
+                    help="extra steps timed with a 1 GiB write between them (evicts L2 / Infinity Cache); 0 = off")
+    return ap.parse_args()
+
+
+def algorithmic(cfg, N, U):
+    """Algorithmic work of each stage for realised local rows N and source
+    tokens with a local pick U."""
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    return {
+        "route": dict(flop=2.0 * T * E * H, bytes=2.0 * T * H + 4.0 * E * H + 4.0 * T * E + 8.0 * T * k),
+        "dispatch": dict(bytes=2.0 * U * H + 2.0 * N * H + 8.0 * T * k + 4.0 * N),
+        "gemm1_gate_up_swiglu": dict(flop=4.0 * N * H * I),
+        "gemm2_down": dict(flop=2.0 * N * I * H),
+        "combine": dict(bytes=2.0 * N * H + 2.0 * T * H + 8.0 * T * k),
+    }
+
+
+def cpu_baseline(inp, sample_tokens):
+    """The CPU oracle, as it stands, on the first `sample_tokens` tokens of the
+    same workload (all of the rank's experts)."""
+    import numpy as np
+    import oracle.moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        cores = int(blas[0]["num_threads"]) if blas else len(os.sched_getaffinity(0))
+        blas_name = blas[0].get("internal_api", "?") if blas else "?"
+    except Exception:  # pragma: no cover
+        cores, blas_name = len(os.sched_getaffinity(0)), "?"
+    cfg = inp.cfg
+    S = min(sample_tokens, cfg.T)
+    x = inp.x[:S]
+    t0 = time.perf_counter()
+    O.oracle_forward(x, inp.w_router, inp.bias, inp.w_gate_up, inp.w_down, cfg.k, cfg.e0, cfg.E_local,
+                     cfg.renormalize)
+    dt = time.perf_counter() - t0
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": S / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {S} of {cfg.T} tokens of {cfg.name}, all {cfg.E_local} local experts, "
+                      f"float64 numpy ({blas_name}), one run of {dt:.1f} s on {cpu}"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's share of the MoE layer; runs on more than one GPU are not part "
+              "of this build (--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import expert_token_routing_amd as M
+    import workloads as W
+
+    cfg = W.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] generating {cfg.name} inputs")
+    inp = W.make_inputs(cfg)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x = bf(inp.x)
+    wr = torch.from_numpy(inp.w_router).to(dev)
+    bias = None if inp.bias is None else torch.from_numpy(inp.bias).to(dev)
+    gu = bf(inp.w_gate_up)
+    dn = bf(inp.w_down)
+    y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(M.forward_workspace_size(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.E_local),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def new_events(n):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n)]
+        for row in evs:
+            for ev in row:
+                ev.record(stream)  # creates the underlying HIP event
+        return evs
+
+    def step(evs):
+        M.moe_forward_profiled(x, wr, bias, gu, dn, cfg.k, cfg.e0, cfg.renormalize, y, ws, evs, stream=stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    wev = new_events(1)
+    for _ in range(args.warmup):
+        step(wev[0])
+    torch.cuda.synchronize()
+
+    evs = new_events(args.steps)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(5)] for i in range(args.steps)])
+    stage_avg = stage_ms.mean(0)
+    log("[bench] stage ms: " + ", ".join(f"{n}={v:.3f}" for n, v in zip(STAGES, stage_avg)))
+
+    cold = None
+    if args.cold_steps > 0:
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cev = new_events(args.cold_steps)
+        torch.cuda.synchronize()
+        for i in range(args.cold_steps):
+            scratch.fill_(i & 0xFF)
+            step(cev[i])
+        torch.cuda.synchronize()
+        cms = np.array([[cev[i][j].elapsed_time(cev[i][j + 1]) for j in range(5)] for i in range(args.cold_steps)])
+        cold = {"ms_per_step": float(cms.sum(1).mean()),
+                "stage_ms": {n: round(float(v), 4) for n, v in zip(STAGES, cms.mean(0))}}
+        del scratch
+
+    # realised routing of the timed steps (identical every step)
+    lay = M.forward_workspace_layout(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.E_local)
+    offs = ws[lay["offsets"]:lay["offsets"] + 4 * (cfg.E_local + 1)].view(torch.int32).cpu().numpy()
+    inv = ws[lay["inv"]:lay["inv"] + 4 * cfg.T * cfg.k].view(torch.int32).reshape(cfg.T, cfg.k).cpu().numpy()
+    N = int(offs[-1])
+    U = int((inv >= 0).any(1).sum())
+    work = algorithmic(cfg, N, U)
+
+    stages = {}
+    for n, ms in zip(STAGES, stage_avg):
+        s = {"us": round(float(ms) * 1e3, 2)}
+        if "flop" in work[n]:
+            s["tflops"] = round(work[n]["flop"] / (ms * 1e-3) / 1e12, 2)
+        if "bytes" in work[n]:
+            s["gbs"] = round(work[n]["bytes"] / (ms * 1e-3) / 1e9, 1)
+        if n.startswith("gemm"):
+            s["frac_mfma_bf16"] = round(s["tflops"] / PEAK_BF16_TFLOPS, 4)
+        if n in ("dispatch", "combine"):
+            s["frac_hbm"] = round(s["gbs"] / PEAK_HBM_GBS, 4)
+        stages[n] = s
+
+    g1 = work["gemm1_gate_up_swiglu"]["flop"] / (stage_avg[2] * 1e-3) / 1e12
+    gemm_ms = stage_avg[2] + stage_avg[3]
+    gemm_tflops = 6.0 * N * cfg.H * cfg.I / (gemm_ms * 1e-3) / 1e12
+    ms_per_step = wall / args.steps * 1e3
+    total_flop = 6.0 * N * cfg.H * cfg.I + 2.0 * cfg.T * cfg.E * cfg.H
+    result = {
+        "metric": METRIC,
+        "value": round(cfg.T * args.steps / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded numpy PCG64, shapes of the named workload; no trained weights)",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "k": cfg.k,
+                   "e0": cfg.e0, "E_local": cfg.E_local, "renormalize": cfg.renormalize,
+                   "parallelism": "one EP rank's share on 1 GPU"},
+        "roofline": {"bound": "mfma", "kernel": "grouped GEMM1 (gate/up + SwiGLU)",
+                     "achieved": round(g1, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(g1 / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "grouped_gemm": {"tflops": round(gemm_tflops, 2), "frac_mfma_bf16": round(gemm_tflops / PEAK_BF16_TFLOPS, 4)},
+        "stages": stages,
+        "layer_tflops": round(total_flop / (ms_per_step * 1e-3) / 1e12, 2),
+        "realised": {"N_local_rows": N, "U_tokens_with_local_pick": U,
+                     "rows_per_local_expert_max": int(np.diff(offs).max()),
+                     "local_experts_empty": int((np.diff(offs) == 0).sum())},
+        "cold": cold,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle on {args.cpu_sample_tokens} tokens")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -17,6 +17,7 @@
 // `offsets` (m-tiles of BM rows per segment x n-tiles) and strides over it.
 // Weights are n-contiguous in memory and are transposed 8 x 8 in registers on
 // their way to LDS, so both MFMA operands are read k-contiguous from LDS.
+#include "gemm_dma.h"
 #include "gemm_tile.h"
 #include "moe_kernels.h"
 
@@ -151,6 +152,154 @@ grouped_gemm_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __re
   }
 }
 
+// Same computation with a deeper memory pipeline, for k a multiple of 64:
+// direct global->LDS loads double buffered (the next k stage is in flight
+// while the current one is multiplied), B read from LDS with transposing
+// reads instead of a register transpose. Tiles go to XCDs in contiguous
+// expert-major ranges (workgroup b runs on XCD b % 8), so the workgroups
+// sharing an expert's weight and row panels share one L2.
+template <int BM, bool SWIGLU>
+__global__ void __launch_bounds__(dma::kThreads)
+grouped_gemm_dma_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __restrict__ offsets, int E_local,
+                        int64_t capacity, const uint16_t* __restrict__ W, int64_t w_expert_stride, int ldw,
+                        uint16_t* __restrict__ C, int ldc, int K, int N, int up_off) {
+  using namespace dma;
+  constexpr int FM = BM / 64;
+  constexpr int FN = 4;
+  constexpr int kAStage = BM * 128;
+  constexpr int kStage = kAStage + kBStageBytes;
+  constexpr int kLoads = BM / 32 + 8;  // DMA instructions per thread per stage
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStage];
+  __shared__ int s_off[kMaxLocal + 1];
+  __shared__ int s_tpre[kMaxLocal + 1];
+  __shared__ int s_tmp[4];
+  MOE_LDS char* lds = (MOE_LDS char*)smem;
+
+  int mt[4];
+  int sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = threadIdx.x * 4 + q;
+    mt[q] = 0;
+    if (i < E_local) {
+      const int64_t a = min<int64_t>(max<int64_t>(offsets[i], 0), capacity);
+      const int64_t b = max<int64_t>(a, min<int64_t>(offsets[i + 1], capacity));
+      s_off[i] = int(a);
+      mt[q] = int((b - a + BM - 1) / BM);
+      if (i == E_local - 1) s_off[E_local] = int(b);
+    }
+    sum += mt[q];
+  }
+  int total_mt;
+  int pre = block_exclusive_scan(sum, s_tmp, total_mt);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = threadIdx.x * 4 + q;
+    if (i < E_local) s_tpre[i] = pre;
+    pre += mt[q];
+  }
+  __syncthreads();
+
+  const int ntn = SWIGLU ? (N + 127) / 128 : (N + 255) / 256;
+  const int total = total_mt * ntn;
+  const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int lane = lane_id();
+  const int nk = K / dma::kBK;
+  // contiguous tile range of this workgroup's XCD
+  const int nxcd = 8;
+  const int xcd = blockIdx.x % nxcd;
+  const int per_xcd = gridDim.x / nxcd;
+  const int lo_t = int((int64_t(total) * xcd) / nxcd);
+  const int hi_t = int((int64_t(total) * (xcd + 1)) / nxcd);
+
+  for (int tile = lo_t + int(blockIdx.x / nxcd); tile < hi_t; tile += per_xcd) {
+    const int gm = tile / ntn;
+    const int nj = tile - gm * ntn;
+    int lo = 0, hi = E_local - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_tpre[mid] <= gm)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const int e = lo;
+    const int r0 = s_off[e] + (gm - s_tpre[e]) * BM;
+    const int rows = min(BM, s_off[e + 1] - r0);
+    const uint16_t* We = W + int64_t(e) * w_expert_stride;
+
+    auto col_of = [&](int s0) -> int {
+      if (SWIGLU) {
+        const int q = s0 & 127;
+        const int oc = nj * 128 + (s0 >> 7) * 64 + (q & 63);
+        if (oc >= N) return 0;
+        return q < 64 ? oc : up_off + oc;
+      } else {
+        const int oc = nj * 256 + s0;
+        return oc < N ? oc : 0;
+      }
+    };
+
+    f32x16 acc[FM][FN];
+    zero_acc(acc);
+    ALoader<BM> la;
+    BLoader lb;
+    la.init(A + int64_t(r0) * lda, lda, rows);
+    lb.init(We, ldw, K, col_of);
+    la.issue(lds, 0);
+    lb.issue(lds + kAStage, 0);
+    FragAddr fa;
+    fa.init(wm * (BM / 2), wn * 128);
+    for (int kt = 0; kt < nk; ++kt) {
+      MOE_LDS char* cur = lds + (kt & 1) * kStage;
+      if (kt + 1 < nk) {
+        MOE_LDS char* nxt = lds + ((kt + 1) & 1) * kStage;
+        la.issue(nxt, (kt + 1) * dma::kBK);
+        lb.issue(nxt + kAStage, (kt + 1) * dma::kBK);
+        wait_vm_barrier<kLoads>();
+      } else {
+        wait_vm_barrier<0>();
+      }
+      dma::mma_stage<FM, FN>(cur, cur + kAStage, fa, acc);
+      wait_lds_barrier();
+    }
+
+    if (SWIGLU) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn) {
+          __builtin_amdgcn_sched_barrier(0);
+          const int col = nj * 128 + wn * 64 + fn * 32 + (lane & 31);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = wm * (BM / 2) + fm * 32 + mfma_c_row(v, lane);
+            if (row < rows && col < N) {
+              const float g = acc[fm][fn][v];
+              const float u = acc[fm][fn + 2][v];
+              const float hv = g / (1.f + __expf(-g)) * u;
+              C[int64_t(r0 + row) * ldc + col] = uint16_t(f32_to_bf16_bits(hv));
+            }
+          }
+        }
+    } else {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          __builtin_amdgcn_sched_barrier(0);
+          const int col = nj * 256 + wn * 128 + fn * 32 + (lane & 31);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = wm * (BM / 2) + fm * 32 + mfma_c_row(v, lane);
+            if (row < rows && col < N)
+              C[int64_t(r0 + row) * ldc + col] = uint16_t(f32_to_bf16_bits(acc[fm][fn][v]));
+          }
+        }
+    }
+  }
+}
+
 namespace {
 constexpr int kFfnBM = 128;
 unsigned persistent_grid(int64_t tiles) {
@@ -158,8 +307,22 @@ unsigned persistent_grid(int64_t tiles) {
 }
 }  // namespace
 
+constexpr int kDmaBM = 256;
+unsigned dma_grid(int64_t tiles) {
+  // a multiple of the 8 XCDs, at most one workgroup per CU
+  const int64_t cus = device_cu_count() / 8 * 8;
+  const int64_t want = std::max<int64_t>(8, std::min<int64_t>(cus, (tiles + 7) / 8 * 8));
+  return unsigned(want);
+}
+
 hipError_t launch_expert_gemm1(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_gate_up, int H,
                                int I, int E_local, int64_t capacity, uint16_t* h, hipStream_t stream) {
+  if (H % dma::kBK == 0) {
+    const int64_t tiles = (ceil_div(capacity, kDmaBM) + E_local) * ceil_div(I, 128);
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<kDmaBM, true>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream,
+                       x_perm, H, offsets, E_local, capacity, w_gate_up, int64_t(H) * 2 * I, 2 * I, h, I, H, I, I);
+    return hipGetLastError();
+  }
   const int64_t mt_bound = ceil_div(capacity, kFfnBM) + E_local;
   const unsigned grid = persistent_grid(mt_bound * ceil_div(I, 128));
   hipLaunchKernelGGL((grouped_gemm_kernel<kFfnBM, true>), dim3(grid), dim3(kThreads), 0, stream, x_perm, H, offsets,
@@ -169,6 +332,12 @@ hipError_t launch_expert_gemm1(const uint16_t* x_perm, const int32_t* offsets, c
 
 hipError_t launch_expert_gemm2(const uint16_t* h, const int32_t* offsets, const uint16_t* w_down, int H, int I,
                                int E_local, int64_t capacity, uint16_t* out, hipStream_t stream) {
+  if (I % dma::kBK == 0) {
+    const int64_t tiles = (ceil_div(capacity, kDmaBM) + E_local) * ceil_div(H, 256);
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<kDmaBM, false>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0,
+                       stream, h, I, offsets, E_local, capacity, w_down, int64_t(I) * H, H, out, H, I, H, 0);
+    return hipGetLastError();
+  }
   const int64_t mt_bound = ceil_div(capacity, kFfnBM) + E_local;
   const unsigned grid = persistent_grid(mt_bound * ceil_div(H, 256));
   hipLaunchKernelGGL((grouped_gemm_kernel<kFfnBM, false>), dim3(grid), dim3(kThreads), 0, stream, h, I, offsets,
