@@ -41,8 +41,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsr1_ep8_share", choices=list(W.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2048,
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16384,
                     help="tokens of the workload the CPU oracle runs on (bounded sample)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before timing, copy a buffer of this many MiB device to device once (a plain copy of "
+                         "known size that scales hardware byte counters); 0 = off")
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="extra steps timed with a 1 GiB write between them (evicts L2 / Infinity Cache); 0 = off")
     return ap.parse_args()
@@ -136,6 +139,16 @@ def main():
 
     def step(evs):
         M.moe_forward_profiled(x, wr, bias, gu, dn, cfg.k, cfg.e0, cfg.renormalize, y, ws, evs, stream=stream)
+
+    if args.copy_calibration_mib > 0:
+        nb = args.copy_calibration_mib << 20
+        src = torch.full((nb,), 7, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {nb} bytes read, {nb} bytes written")
+        del src, dst
 
     log(f"[bench] warmup {args.warmup}")
     wev = new_events(1)

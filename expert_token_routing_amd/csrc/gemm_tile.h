@@ -120,8 +120,9 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[FM][FN]) {
       for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
 }
 
-// Exclusive scan over a 256-thread block; returns the prefix, writes the total.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* s_tmp /* >= 4 ints */, int& total) {
+// Exclusive scan over a block of NT threads; returns the prefix, writes the total.
+template <int NT = 256>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* s_tmp /* >= NT/64 ints */, int& total) {
   const int lane = lane_id();
   const int w = threadIdx.x >> 6;
   int inc = v;
@@ -135,7 +136,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_tmp /* >= 4 in
   int base = 0;
   int tot = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NT / 64; ++i) {
     const int s = s_tmp[i];
     if (i < w) base += s;
     tot += s;

@@ -2,7 +2,7 @@
 // the one-stream forward pass. Every check runs on the host before any launch.
 #include <mutex>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "moe_kernels.h"
 
 namespace moe {
