@@ -51,16 +51,20 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic(cfg, N, U):
+def algorithmic(cfg, N, U, fused_gather=True):
     """Algorithmic work of each stage for realised local rows N and source
-    tokens with a local pick U."""
+    tokens with a local pick U. In the fused forward, dispatch only builds the
+    tables (GEMM1 reads the token rows in place); the row-moving dispatch of
+    the standalone entry point is `dispatch_rows`."""
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    rows = dict(bytes=2.0 * U * H + 2.0 * N * H + 8.0 * T * k + 4.0 * N)
     return {
         "route": dict(flop=2.0 * T * E * H, bytes=2.0 * T * H + 4.0 * E * H + 4.0 * T * E + 8.0 * T * k),
-        "dispatch": dict(bytes=2.0 * U * H + 2.0 * N * H + 8.0 * T * k + 4.0 * N),
+        "dispatch": dict(bytes=8.0 * T * k + 4.0 * N) if fused_gather else rows,
         "gemm1_gate_up_swiglu": dict(flop=4.0 * N * H * I),
         "gemm2_down": dict(flop=2.0 * N * I * H),
         "combine": dict(bytes=2.0 * N * H + 2.0 * T * H + 8.0 * T * k),
+        "dispatch_rows": rows,
     }
 
 
@@ -188,7 +192,30 @@ def main():
     inv = ws[lay["inv"]:lay["inv"] + 4 * cfg.T * cfg.k].view(torch.int32).reshape(cfg.T, cfg.k).cpu().numpy()
     N = int(offs[-1])
     U = int((inv >= 0).any(1).sum())
-    work = algorithmic(cfg, N, U)
+    fused = cfg.H % 32 == 0 and cfg.T * cfg.H * 2 < 2 ** 31
+    work = algorithmic(cfg, N, U, fused)
+
+    # the standalone dispatch entry point (tables + rows moved into x_perm),
+    # timed on its own with the forward's top-k ids
+    idx = ws[lay["topk_idx"]:lay["topk_idx"] + 4 * cfg.T * cfg.k].view(torch.int32).reshape(cfg.T, cfg.k)
+    cap = cfg.capacity
+    d_out = dict(counts=torch.empty(cfg.E, dtype=torch.int32, device=dev),
+                 offsets=torch.empty(cfg.E_local + 1, dtype=torch.int32, device=dev),
+                 perm_src=torch.empty(cap, dtype=torch.int32, device=dev),
+                 inv=torch.empty(cfg.T * cfg.k, dtype=torch.int32, device=dev),
+                 x_perm=torch.empty((cap, cfg.H), dtype=torch.bfloat16, device=dev))
+    d_ws = torch.empty(M.lib().moe_dispatch_workspace_size(cfg.T, cfg.E, cfg.k), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        M.moe_dispatch(x, idx, cfg.E, cfg.e0, cfg.E_local, workspace=d_ws, **d_out)
+    nd = max(5, args.steps // 2)
+    dev_ev = [torch.cuda.Event(enable_timing=True) for _ in range(nd + 1)]
+    dev_ev[0].record(stream)
+    for i in range(nd):
+        M.moe_dispatch(x, idx, cfg.E, cfg.e0, cfg.E_local, workspace=d_ws, **d_out)
+        dev_ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    d_ms = float(np.mean([dev_ev[i].elapsed_time(dev_ev[i + 1]) for i in range(nd)]))
+    del d_out, d_ws
 
     stages = {}
     for n, ms in zip(STAGES, stage_avg):
@@ -202,6 +229,11 @@ def main():
         if n in ("dispatch", "combine"):
             s["frac_hbm"] = round(s["gbs"] / PEAK_HBM_GBS, 4)
         stages[n] = s
+    if fused:
+        stages["dispatch"]["note"] = "tables only; GEMM1 gathers the token rows in place"
+    d_gbs = work["dispatch_rows"]["bytes"] / (d_ms * 1e-3) / 1e9
+    dispatch_rows = {"us": round(d_ms * 1e3, 2), "gbs": round(d_gbs, 1), "frac_hbm": round(d_gbs / PEAK_HBM_GBS, 4),
+                     "note": "moe_dispatch entry point (tables + token rows copied to x_perm), timed alone"}
 
     g1 = work["gemm1_gate_up_swiglu"]["flop"] / (stage_avg[2] * 1e-3) / 1e12
     gemm_ms = stage_avg[2] + stage_avg[3]
@@ -229,6 +261,7 @@ def main():
                      "frac": round(g1 / PEAK_BF16_TFLOPS, 4), "traffic": None},
         "grouped_gemm": {"tflops": round(gemm_tflops, 2), "frac_mfma_bf16": round(gemm_tflops / PEAK_BF16_TFLOPS, 4)},
         "stages": stages,
+        "dispatch_rows": dispatch_rows,
         "layer_tflops": round(total_flop / (ms_per_step * 1e-3) / 1e12, 2),
         "realised": {"N_local_rows": N, "U_tokens_with_local_pick": U,
                      "rows_per_local_expert_max": int(np.diff(offs).max()),

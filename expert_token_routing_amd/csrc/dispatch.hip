@@ -170,9 +170,9 @@ dispatch_copy_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__
   }
 }
 
-hipError_t launch_dispatch(const uint16_t* x, const int32_t* topk_idx, int T, int H, int E, int k, int e0,
-                           int E_local, int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv,
-                           uint16_t* x_perm, int32_t* chunk_table, hipStream_t stream) {
+hipError_t launch_dispatch_index(const int32_t* topk_idx, int T, int E, int k, int e0, int E_local, int32_t* counts,
+                                 int32_t* offsets, int32_t* perm_src, int32_t* inv, int32_t* chunk_table,
+                                 hipStream_t stream) {
   const int nchunks = int(ceil_div(T, kChunk));
   const unsigned wgs = unsigned(ceil_div(nchunks, 4));
   hipLaunchKernelGGL(dispatch_hist_kernel, dim3(wgs), dim3(kThreads), size_t(4) * E * sizeof(int), stream,
@@ -198,7 +198,15 @@ hipError_t launch_dispatch(const uint16_t* x, const int32_t* topk_idx, int T, in
   else
     MOE_INDEX_LAUNCH(32);
 #undef MOE_INDEX_LAUNCH
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const uint16_t* x, const int32_t* topk_idx, int T, int H, int E, int k, int e0,
+                           int E_local, int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv,
+                           uint16_t* x_perm, int32_t* chunk_table, hipStream_t stream) {
+  hipError_t err =
+      launch_dispatch_index(topk_idx, T, E, k, e0, E_local, counts, offsets, perm_src, inv, chunk_table, stream);
+  if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_copy_kernel, dim3(unsigned(ceil_div(T, 4))), dim3(kThreads), 0, stream, x, inv, T,
                      H, k, x_perm);
   return hipGetLastError();

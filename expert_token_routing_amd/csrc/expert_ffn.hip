@@ -167,7 +167,8 @@ namespace dmaffn {
 template <int LOAD_BM, int FM, bool SWIGLU>
 __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __restrict__ A, int lda, int r0,
                                          int rows, const uint16_t* __restrict__ We, int ldw, int K, int N,
-                                         int up_off, int nj, uint16_t* __restrict__ C, int ldc) {
+                                         int up_off, int nj, uint16_t* __restrict__ C, int ldc,
+                                         const int32_t* __restrict__ gather_src, int gather_k, int gather_rows) {
   using namespace dma;
   constexpr int FN = 2;
   constexpr int kAStage = LOAD_BM * kARowBytes;
@@ -194,7 +195,10 @@ __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __re
   zero_acc(acc);
   ALoader<LOAD_BM> la;
   BLoader lb;
-  la.init(A + int64_t(r0) * lda, lda, rows);
+  if (gather_src != nullptr)  // A rows are token vectors: row r0+r is token src[r0+r] / k
+    la.init_gather(A, lda, gather_rows, rows, [&](int r) { return gather_src[r0 + r] / gather_k; });
+  else
+    la.init(A + int64_t(r0) * lda, lda, rows);
   lb.init(We, ldw, K, col_of);
   // ring of kStages buffers: stages kt+1 .. kt+kStages-1 in flight while
   // stage kt is multiplied
@@ -290,7 +294,8 @@ template <bool SWIGLU>
 __global__ void __launch_bounds__(dma::kThreads)
 grouped_gemm_dma_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __restrict__ offsets, int E_local,
                         int64_t capacity, const uint16_t* __restrict__ W, int64_t w_expert_stride, int ldw,
-                        uint16_t* __restrict__ C, int ldc, int K, int N, int up_off) {
+                        uint16_t* __restrict__ C, int ldc, int K, int N, int up_off,
+                        const int32_t* __restrict__ gather_src, int gather_k, int gather_rows) {
   using namespace dma;
   __shared__ __attribute__((aligned(1024))) char smem[kStages * (256 * kARowBytes + kBStageBytes)];
   __shared__ int s_off[kMaxLocal + 1];
@@ -357,7 +362,7 @@ grouped_gemm_dma_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* 
     const int r0 = seg0 + mi * 256;
     const int rows = min(256, __builtin_amdgcn_readfirstlane(s_off[e + 1]) - r0);
     dmaffn::run_tile<256, 4, SWIGLU>(lds, A, lda, r0, rows, W + int64_t(e) * w_expert_stride, ldw, K, N, up_off, nj,
-                                      C, ldc);
+                                      C, ldc, gather_src, gather_k, gather_rows);
   }
 }
 
@@ -380,7 +385,8 @@ hipError_t launch_expert_gemm1(const uint16_t* x_perm, const int32_t* offsets, c
   if (H % dma::kBK == 0) {
     const int64_t tiles = (ceil_div(capacity, 256) + 2 * E_local) * ceil_div(I, 128);
     hipLaunchKernelGGL((grouped_gemm_dma_kernel<true>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream,
-                       x_perm, H, offsets, E_local, capacity, w_gate_up, int64_t(H) * 2 * I, 2 * I, h, I, H, I, I);
+                       x_perm, H, offsets, E_local, capacity, w_gate_up, int64_t(H) * 2 * I, 2 * I, h, I, H, I, I,
+                       nullptr, 1, 0);
     return hipGetLastError();
   }
   const int64_t mt_bound = ceil_div(capacity, kFfnBM) + E_local;
@@ -395,13 +401,25 @@ hipError_t launch_expert_gemm2(const uint16_t* h, const int32_t* offsets, const 
   if (I % dma::kBK == 0) {
     const int64_t tiles = (ceil_div(capacity, 256) + 2 * E_local) * ceil_div(H, 256);
     hipLaunchKernelGGL((grouped_gemm_dma_kernel<false>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0,
-                       stream, h, I, offsets, E_local, capacity, w_down, int64_t(I) * H, H, out, H, I, H, 0);
+                       stream, h, I, offsets, E_local, capacity, w_down, int64_t(I) * H, H, out, H, I, H, 0, nullptr, 1,
+                       0);
     return hipGetLastError();
   }
   const int64_t mt_bound = ceil_div(capacity, kFfnBM) + E_local;
   const unsigned grid = persistent_grid(mt_bound * ceil_div(H, 256));
   hipLaunchKernelGGL((grouped_gemm_kernel<kFfnBM, false>), dim3(grid), dim3(kThreads), 0, stream, h, I, offsets,
                      E_local, capacity, w_down, int64_t(I) * H, H, out, H, I, H, 0);
+  return hipGetLastError();
+}
+
+bool expert_gemm1_can_gather(int T, int H) { return H % dma::kBK == 0 && int64_t(T) * H * 2 < (int64_t(1) << 31); }
+
+hipError_t launch_expert_gemm1_gather(const uint16_t* x, const int32_t* perm_src, int T, int k, const int32_t* offsets,
+                                      const uint16_t* w_gate_up, int H, int I, int E_local, int64_t capacity,
+                                      uint16_t* h, hipStream_t stream) {
+  const int64_t tiles = (ceil_div(capacity, 256) + 2 * E_local) * ceil_div(I, 128);
+  hipLaunchKernelGGL((grouped_gemm_dma_kernel<true>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream, x, H,
+                     offsets, E_local, capacity, w_gate_up, int64_t(H) * 2 * I, 2 * I, h, I, H, I, I, perm_src, k, T);
   return hipGetLastError();
 }
 

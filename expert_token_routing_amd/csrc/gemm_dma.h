@@ -108,6 +108,21 @@ struct ALoader {
       voff[i] = uint32_t(min(r, rows - 1)) * uint32_t(lda) * 2u + 16u * uint32_t(c);
     }
   }
+  // Same tile, but tile row r is row src_row(r) of the whole matrix `base`
+  // (rows.. rows_total) -- a gather, used to read token vectors in place.
+  template <typename SrcRow>
+  __device__ __forceinline__ void init_gather(const uint16_t* base, int lda, int rows_total, int rows,
+                                              SrcRow src_row) {
+    rsrc = buffer_rsrc(base, int64_t(rows_total) * lda * 2);
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int r = 16 * (i * kWaves + w) + (lane >> 2);
+      const int c = (lane & 3) ^ ((r >> 2) & 3);
+      voff[i] = uint32_t(src_row(min(r, rows - 1))) * uint32_t(lda) * 2u + 16u * uint32_t(c);
+    }
+  }
   __device__ __forceinline__ void issue(MOE_LDS char* As, int k0) const {
     const int w = threadIdx.x >> 6;
 #pragma unroll

@@ -214,11 +214,17 @@ static int forward_impl(const moe_bf16* x, const float* w_router, const float* b
     err = launch_route(x, w_router, bias, T, H, E, k, renormalize, logits, topk_idx, topk_w,
                        static_cast<uint16_t*>(at(L.planes)), stream);
   if (err == hipSuccess) err = mark(1);
+  // GEMM1 reads the token vectors in place when it can, so dispatch only
+  // builds the tables; otherwise the rows are copied out first.
+  const bool gather = expert_gemm1_can_gather(T, H);
   if (err == hipSuccess)
-    err = launch_dispatch(x, topk_idx, T, H, E, k, e0, E_local, counts, offsets, perm_src, inv, x_perm, chunks,
-                          stream);
+    err = gather ? launch_dispatch_index(topk_idx, T, E, k, e0, E_local, counts, offsets, perm_src, inv, chunks, stream)
+                 : launch_dispatch(x, topk_idx, T, H, E, k, e0, E_local, counts, offsets, perm_src, inv, x_perm,
+                                   chunks, stream);
   if (err == hipSuccess) err = mark(2);
-  if (err == hipSuccess) err = launch_expert_gemm1(x_perm, offsets, w_gate_up, H, I, E_local, cap, h, stream);
+  if (err == hipSuccess)
+    err = gather ? launch_expert_gemm1_gather(x, perm_src, T, k, offsets, w_gate_up, H, I, E_local, cap, h, stream)
+                 : launch_expert_gemm1(x_perm, offsets, w_gate_up, H, I, E_local, cap, h, stream);
   if (err == hipSuccess) err = mark(3);
   if (err == hipSuccess) err = launch_expert_gemm2(h, offsets, w_down, H, I, E_local, cap, out, stream);
   if (err == hipSuccess) err = mark(4);

@@ -34,6 +34,19 @@ hipError_t launch_expert_gemm1(const uint16_t* x_perm, const int32_t* offsets, c
 hipError_t launch_expert_gemm2(const uint16_t* h, const int32_t* offsets, const uint16_t* w_down, int H, int I,
                                int E_local, int64_t capacity, uint16_t* out, hipStream_t stream);
 
+// GEMM1 reading the token vectors of x in place (row n of a segment is token
+// perm_src[n] / k) instead of a dispatched copy; usable when
+// expert_gemm1_can_gather(T, H).
+bool expert_gemm1_can_gather(int T, int H);
+hipError_t launch_expert_gemm1_gather(const uint16_t* x, const int32_t* perm_src, int T, int k, const int32_t* offsets,
+                                      const uint16_t* w_gate_up, int H, int I, int E_local, int64_t capacity,
+                                      uint16_t* h, hipStream_t stream);
+
+// Dispatch without the row copy (counts, offsets, perm_src, inv only).
+hipError_t launch_dispatch_index(const int32_t* topk_idx, int T, int E, int k, int e0, int E_local, int32_t* counts,
+                                 int32_t* offsets, int32_t* perm_src, int32_t* inv, int32_t* chunk_table,
+                                 hipStream_t stream);
+
 // Weighted top-k sum in token order.
 hipError_t launch_combine(const uint16_t* expert_out, const int32_t* inv, const float* topk_w, int T, int H, int k,
                           uint16_t* y, hipStream_t stream);

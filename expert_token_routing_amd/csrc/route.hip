@@ -12,6 +12,7 @@
 // bf16 x bf16 product is exact in float32, and the three products are
 // accumulated in float32. This costs three bf16 MFMAs per product instead of
 // one float32 FMA, which the matrix cores run several times faster.
+#include "gemm_dma.h"
 #include "gemm_tile.h"
 #include "moe_kernels.h"
 
@@ -92,6 +93,133 @@ route_logits_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
       }
     }
 }
+
+// Same logits through the direct-to-LDS pipeline (H a multiple of 32): tiles
+// of 128 tokens x 128 experts, 8 waves of 64 x 32, a ring of four 32-deep
+// stages holding the token rows and the three weight planes, all k-contiguous
+// rows in the swizzled layout.
+namespace routedma {
+
+constexpr int kBM = 128, kBN = 128, kFM = 2, kPlanes = 3;
+constexpr int kRowStage = 128 * dma::kARowBytes;                  // 8 KiB per 128-row operand
+constexpr int kStage = kRowStage * (1 + kPlanes);                  // tokens + 3 planes
+constexpr int kLoads = (1 + kPlanes) * dma::ALoader<128>::kPer;    // DMA instructions per thread per stage
+
+__global__ void __launch_bounds__(dma::kThreads)
+route_logits_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes,
+                        const float* __restrict__ bias, float* __restrict__ logits, int T, int H, int E) {
+  using namespace dma;
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kStage];
+  MOE_LDS char* lds = (MOE_LDS char*)smem;
+  const int t0 = blockIdx.x * kBM;
+  const int n0 = blockIdx.y * kBN;
+  const int w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
+  const int lane = lane_id();
+  const int nk = H / dma::kBK;
+  const int64_t plane = int64_t(E) * H;
+
+  ALoader<128> la, lb[kPlanes];
+  la.init(x + int64_t(t0) * H, H, min(kBM, T - t0));
+#pragma unroll
+  for (int p = 0; p < kPlanes; ++p) lb[p].init(planes + p * plane + int64_t(n0) * H, H, min(kBN, E - n0));
+  auto issue = [&](MOE_LDS char* st, int k0) {
+    la.issue(st, k0);
+#pragma unroll
+    for (int p = 0; p < kPlanes; ++p) lb[p].issue(st + (1 + p) * kRowStage, k0);
+  };
+  // fragment offsets: A rows wm*64 + fm*32 + lane%32, B rows wn*32 + lane%32,
+  // both in the swizzled k-contiguous row layout
+  const int khalf = lane >> 5;
+  const int ma = wm * 64 + (lane & 31);
+  const int mb = wn * 32 + (lane & 31);
+  uint32_t aoff[2], boff[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    aoff[ks] = uint32_t(ma * kARowBytes + 16 * ((2 * ks + khalf) ^ ((ma >> 2) & 3)));
+    boff[ks] = uint32_t(mb * kARowBytes + 16 * ((2 * ks + khalf) ^ ((mb >> 2) & 3)));
+  }
+  struct F {
+    u32x4 a[kFM];
+    u32x4 b[kPlanes];
+  };
+  auto load = [&](const MOE_LDS char* st, int ks, F& f) {
+#pragma unroll
+    for (int fm = 0; fm < kFM; ++fm)
+      f.a[fm] = *reinterpret_cast<const MOE_LDS u32x4*>(st + aoff[ks] + fm * 32 * kARowBytes);
+#pragma unroll
+    for (int p = 0; p < kPlanes; ++p)
+      f.b[p] = *reinterpret_cast<const MOE_LDS u32x4*>(st + (1 + p) * kRowStage + boff[ks]);
+  };
+  f32x16 acc[kFM];
+#pragma unroll
+  for (int fm = 0; fm < kFM; ++fm)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[fm][v] = 0.f;
+  auto mma = [&](const F& f) {
+#pragma unroll
+    for (int p = 0; p < kPlanes; ++p)
+#pragma unroll
+      for (int fm = 0; fm < kFM; ++fm) acc[fm] = mfma32x32x16(f.a[fm], f.b[p], acc[fm]);
+  };
+  auto interleave = [&]() {
+#pragma unroll
+    for (int i = 0; i < kFM * kPlanes; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < kFM + kPlanes) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+
+#pragma unroll
+  for (int p = 0; p < kStages - 1; ++p)
+    if (p < nk) issue(lds + p * kStage, p * dma::kBK);
+  {
+    const int ahead0 = min(kStages - 2, nk - 1);
+    if (ahead0 >= 2)
+      wait_vm_barrier<2 * kLoads>();
+    else if (ahead0 == 1)
+      wait_vm_barrier<kLoads>();
+    else
+      wait_vm_barrier<0>();
+  }
+  F f0, f1;
+  load(lds, 0, f0);
+  for (int kt = 0; kt < nk; ++kt) {
+    MOE_LDS char* cur = lds + (kt % kStages) * kStage;
+    if (kt + kStages - 1 < nk) issue(lds + ((kt + kStages - 1) % kStages) * kStage, (kt + kStages - 1) * dma::kBK);
+    load(cur, 1, f1);
+    mma(f0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) {
+      wait_lgkm0();
+      const int ahead = min(kStages - 2, nk - 2 - kt);
+      if (ahead >= 2)
+        wait_vm_barrier<2 * kLoads>();
+      else if (ahead == 1)
+        wait_vm_barrier<kLoads>();
+      else
+        wait_vm_barrier<0>();
+    }
+    MOE_LDS char* nx = lds + ((kt + 1) % kStages) * kStage;
+    load(nx, 0, f0);
+    mma(f1);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  wait_lgkm0();
+
+  const int e = n0 + mb;
+  const float b = (bias != nullptr && e < E) ? bias[e] : 0.f;
+#pragma unroll
+  for (int fm = 0; fm < kFM; ++fm)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int t = t0 + wm * 64 + fm * 32 + mfma_c_row(v, lane);
+      if (t < T && e < E) logits[int64_t(t) * E + e] = acc[fm][v] + b;
+    }
+}
+
+}  // namespace routedma
 
 // One wave per token: top-k by (logit descending, expert id ascending), then
 // softmax weights. Lane l holds experts l, l+64, ... (EPL per lane).
@@ -180,7 +308,11 @@ hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b
   }
   {
     dim3 grid(unsigned((T + 127) / 128), unsigned((E + 127) / 128));
-    hipLaunchKernelGGL(route_logits_kernel, grid, dim3(kThreads), 0, stream, x, planes, bias, logits, T, H, E);
+    if (H % dma::kBK == 0)
+      hipLaunchKernelGGL(routedma::route_logits_dma_kernel, grid, dim3(dma::kThreads), 0, stream, x, planes, bias,
+                         logits, T, H, E);
+    else
+      hipLaunchKernelGGL(route_logits_kernel, grid, dim3(kThreads), 0, stream, x, planes, bias, logits, T, H, E);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
