@@ -49,25 +49,38 @@ combine_kernel(const uint16_t* __restrict__ expert_out, const int32_t* __restric
   const float init = nl > 0 ? -0.f : 0.f;
   const int nv = H / 8;
   u32x4* dst = reinterpret_cast<u32x4*>(y + int64_t(t) * H);
-  for (int v = lane; v < nv; v += 64) {
-    float acc[8];
+  // U vectors per lane per pass; all of a pass's loads are issued before the
+  // first one is used, so each lane keeps up to U * nl loads in flight.
+  constexpr int U = 2;
+  for (int v0 = lane; v0 < nv; v0 += 64 * U) {
+    u32x4 q[KMAX][U];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = init;
+    for (int j = 0; j < KMAX; ++j)
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      if (j < nl) {
-        const u32x4 q = reinterpret_cast<const u32x4*>(expert_out + int64_t(rows[j]) * H)[v];
+      for (int u = 0; u < U; ++u)
+        if (j < nl && v0 + 64 * u < nv)
+          q[j][u] = reinterpret_cast<const u32x4*>(expert_out + int64_t(rows[j]) * H)[v0 + 64 * u];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] = fmaf(wts[j], bf16_lo(q[i]), acc[2 * i]);
-          acc[2 * i + 1] = fmaf(wts[j], bf16_hi(q[i]), acc[2 * i + 1]);
+    for (int u = 0; u < U; ++u) {
+      if (v0 + 64 * u >= nv) break;
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = init;
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (j < nl) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = fmaf(wts[j], bf16_lo(q[j][u][i]), acc[2 * i]);
+            acc[2 * i + 1] = fmaf(wts[j], bf16_hi(q[j][u][i]), acc[2 * i + 1]);
+          }
         }
       }
-    }
-    u32x4 o;
+      u32x4 o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-    dst[v] = o;
+      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+      dst[v0 + 64 * u] = o;
+    }
   }
 }
 

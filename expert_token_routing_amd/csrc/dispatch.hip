@@ -68,6 +68,7 @@ dispatch_index_kernel(const int32_t* __restrict__ topk_idx, const int32_t* __res
                       const int32_t* __restrict__ counts, int T, int k, int e0, int E_local, int nchunks,
                       int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src, int32_t* __restrict__ inv) {
   __shared__ int s_seg[1024 + 1];
+  __shared__ int s_base[4][1024];
   __shared__ int s_tmp[4];
   // Segment starts: exclusive scan of the local experts' counts (4 per thread).
   int cnt[4];
@@ -91,9 +92,15 @@ dispatch_index_kernel(const int32_t* __restrict__ topk_idx, const int32_t* __res
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= E_local; i += kThreads) offsets[i] = s_seg[i];
 
-  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (c >= nchunks) return;
+  const int wv = threadIdx.x >> 6;
+  const int c = blockIdx.x * 4 + wv;
   const int lane = lane_id();
+  // This chunk's offset inside every local expert's segment, staged in LDS so
+  // that the loop below reads no global memory.
+  if (c < nchunks)
+    for (int i = lane; i < E_local; i += 64) s_base[wv][i] = chunk_base[int64_t(e0 + i) * nchunks + c];
+  __syncthreads();
+  if (c >= nchunks) return;
   const int t = c * kChunk + lane;
   const bool valid = t < T;
   int ev[KMAX];
@@ -118,7 +125,7 @@ dispatch_index_kernel(const int32_t* __restrict__ topk_idx, const int32_t* __res
 #pragma unroll
     for (int j = KMAX - 1; j >= 0; --j)
       if ((pend >> j) & 1u) first = ev[j];
-    const int e_lead = shfl(first, leader);
+    const int e_lead = __builtin_amdgcn_readlane(first, leader);
     int js = -1;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
@@ -126,7 +133,7 @@ dispatch_index_kernel(const int32_t* __restrict__ topk_idx, const int32_t* __res
     const uint64_t mask = ballot(js >= 0);
     if (js >= 0) {
       const int rank = __popcll(mask & lanemask_lt());
-      const int row = s_seg[e_lead - e0] + chunk_base[int64_t(e_lead) * nchunks + c] + rank;
+      const int row = s_seg[e_lead - e0] + s_base[wv][e_lead - e0] + rank;
       const int64_t slot = int64_t(t) * k + js;
       perm_src[row] = int32_t(slot);
       inv[slot] = row;

@@ -111,7 +111,8 @@ int moe_route(const moe_bf16* x, const float* w_router, const float* bias, int T
   int st = check_route_dims(T, H, E, k);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
-  if (!x || !w_router || !logits || !topk_idx || !topk_w || !aligned16(x)) return MOE_ERR_INVALID_ARG;
+  if (!x || !w_router || !logits || !topk_idx || !topk_w || !aligned16(x) || !aligned16(w_router))
+    return MOE_ERR_INVALID_ARG;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0 ||
       workspace_bytes < moe_route_workspace_size(T, H, E, k))
     return MOE_ERR_WORKSPACE;
@@ -189,7 +190,8 @@ static int forward_impl(const moe_bf16* x, const float* w_router, const float* b
   if (min_capacity(T, k, E_local) >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !w_router || !w_gate_up || !w_down || !y) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(y))
+    return MOE_ERR_INVALID_ARG;
   const ForwardLayout L = forward_layout(T, H, I, E, k, E_local);
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0 || workspace_bytes < L.total)
     return MOE_ERR_WORKSPACE;

@@ -1,6 +1,8 @@
 // Device-side building blocks shared by the MoE kernels (gfx950 / CDNA4).
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -78,6 +80,24 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
   return v;
+}
+// Maximum over the wave, returned uniformly: DPP steps within each row of 16
+// lanes (swap neighbours, swap pairs, mirror halves of 8, mirror the 16),
+// then the four row results read as scalars. No LDS traffic.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  auto step = [](float x, auto ctrl) {
+    constexpr int c = decltype(ctrl)::value;
+    return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), c, 0xF, 0xF, false)));
+  };
+  v = step(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+  v = step(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+  v = step(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  v = step(v, std::integral_constant<int, 0x140>{});  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

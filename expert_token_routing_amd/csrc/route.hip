@@ -19,18 +19,27 @@
 namespace moe {
 
 // w (float32) -> hi, mid, lo (bf16 planes of n elements each), hi+mid+lo == w.
+// Four elements per thread (n is a multiple of 8): one 16-byte load, three
+// 8-byte stores.
 __global__ void route_split_kernel(const float* __restrict__ w, uint16_t* __restrict__ planes, int64_t n) {
+  const int64_t n4 = n / 4;
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
-    const float x = w[i];
-    const uint32_t hi = __float_as_uint(x) >> 16;
-    const float r1 = x - __uint_as_float(hi << 16);
-    const uint32_t mid = __float_as_uint(r1) >> 16;
-    const float r2 = r1 - __uint_as_float(mid << 16);
-    const uint32_t lo = __float_as_uint(r2) >> 16;
-    planes[i] = uint16_t(hi);
-    planes[n + i] = uint16_t(mid);
-    planes[2 * n + i] = uint16_t(lo);
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const float4 x4 = reinterpret_cast<const float4*>(w)[i];
+    const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
+    uint32_t hi[4], mid[4], lo[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float x = xs[q];
+      hi[q] = __float_as_uint(x) >> 16;
+      const float r1 = x - __uint_as_float(hi[q] << 16);
+      mid[q] = __float_as_uint(r1) >> 16;
+      const float r2 = r1 - __uint_as_float(mid[q] << 16);
+      lo[q] = __float_as_uint(r2) >> 16;
+    }
+    reinterpret_cast<uint2*>(planes)[i] = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+    reinterpret_cast<uint2*>(planes + n)[i] = make_uint2(mid[0] | (mid[1] << 16), mid[2] | (mid[3] << 16));
+    reinterpret_cast<uint2*>(planes + 2 * n)[i] = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
   }
 }
 
@@ -222,7 +231,9 @@ route_logits_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
 }  // namespace routedma
 
 // One wave per token: top-k by (logit descending, expert id ascending), then
-// softmax weights. Lane l holds experts l, l+64, ... (EPL per lane).
+// softmax weights. Lane l holds experts l, l+64, ... (EPL per lane). Each of
+// the k rounds takes the wave maximum of the experts not yet taken (DPP, no
+// LDS) and then the lowest expert id holding it (one ballot per EPL slot).
 template <int EPL>
 __global__ void __launch_bounds__(kThreads)
 route_topk_kernel(const float* __restrict__ logits, int T, int E, int k, int renormalize,
@@ -232,49 +243,43 @@ route_topk_kernel(const float* __restrict__ logits, int T, int E, int k, int ren
   if (t >= T) return;
   const float* row = logits + int64_t(t) * E;
   float v[EPL];
-  float m = -INFINITY;
+  uint32_t live = 0;  // bit i: expert lane + 64 i exists and is not taken yet
+  float lm = -INFINITY;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + 64 * i;
     v[i] = e < E ? row[e] : -INFINITY;
-    m = fmaxf(m, v[i]);
+    if (e < E) {
+      live |= 1u << i;
+      lm = fmaxf(lm, v[i]);
+    }
   }
-  m = wave_max(m);
+  const float m = wave_max_dpp(lm);
 
   float den_all = 0.f;
   if (!renormalize) {
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
-      if (lane + 64 * i < E) s += expf(v[i] - m);
+      if ((live >> i) & 1u) s += expf(v[i] - m);
     den_all = wave_sum(s);
   }
 
-  uint32_t taken = 0;
   int my_e = 0;
   float my_v = 0.f;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
+    float cm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if ((live >> i) & 1u) cm = fmaxf(cm, v[i]);
+    const float bv = wave_max_dpp(cm);
     int be = 0x7FFFFFFF;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane + 64 * i;
-      const bool ok = e < E && !((taken >> i) & 1u);
-      if (ok && (v[i] > bv || (v[i] == bv && e < be))) {
-        bv = v[i];
-        be = e;
-      }
+    for (int i = EPL - 1; i >= 0; --i) {
+      const uint64_t hit = ballot(((live >> i) & 1u) && v[i] == bv);
+      if (hit) be = 64 * i + (__ffsll((unsigned long long)hit) - 1);
     }
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-      const float ov = shfl_xor(bv, s);
-      const int oe = shfl_xor(be, s);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if (lane == (be & 63)) taken |= 1u << (be >> 6);
+    if (lane == (be & 63)) live &= ~(1u << (be >> 6));
     if (lane == j) {
       my_e = be;
       my_v = bv;
@@ -301,7 +306,7 @@ hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b
   const int64_t n = int64_t(E) * H;
   {
     const int threads = 256;
-    const int64_t blocks = std::min<int64_t>((n + threads - 1) / threads, 4096);
+    const int64_t blocks = std::min<int64_t>((n / 4 + threads - 1) / threads, 4096);
     hipLaunchKernelGGL(route_split_kernel, dim3(unsigned(blocks)), dim3(threads), 0, stream, w_router, planes, n);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -36,6 +36,9 @@
  *   - T = 0 is valid: the call returns MOE_OK and launches nothing.
  *   - supported sizes: 1 <= k <= min(E, 32); E <= 1024; H and I multiples
  *     of 8 (16-byte vectors); T * k < 2^31.
+ *   - matrix pointers (x, w_router, w_gate_up, w_down, x_perm, h, out,
+ *     expert_out, y) are 16-byte aligned; a misaligned one is
+ *     MOE_ERR_INVALID_ARG.
  */
 #ifndef MOE_H_
 #define MOE_H_

@@ -75,6 +75,7 @@ def _route(**kw):
     (dict(x=None), M.MOE_ERR_INVALID_ARG),
     (dict(logits=None), M.MOE_ERR_INVALID_ARG),
     (dict(x=FAKE_ODD), M.MOE_ERR_INVALID_ARG),
+    (dict(w=FAKE_ODD), M.MOE_ERR_INVALID_ARG),   # router weight read as 16-byte vectors
     (dict(ws=None), M.MOE_ERR_WORKSPACE),
     (dict(wsb=16), M.MOE_ERR_WORKSPACE),
     (dict(ws=ctypes.c_void_p(0x100010)), M.MOE_ERR_WORKSPACE),  # not 256-byte aligned
@@ -148,6 +149,7 @@ def _forward(**kw):
     (dict(e0=1), M.MOE_ERR_INVALID_ARG),
     (dict(y=None), M.MOE_ERR_INVALID_ARG),
     (dict(gu=FAKE_ODD), M.MOE_ERR_INVALID_ARG),
+    (dict(w=FAKE_ODD), M.MOE_ERR_INVALID_ARG),
     (dict(wsb=1024), M.MOE_ERR_WORKSPACE),
     (dict(ws=None), M.MOE_ERR_WORKSPACE),
     (dict(k=0), M.MOE_ERR_INVALID_ARG),

@@ -266,6 +266,33 @@ def test_pages_dispatch_examples(fixture):
             assert np.array_equal(yb[t], xf[t] if local else np.zeros(H))
 
 
+@pytest.mark.parametrize("E,k,renorm", [(4, 4, 1), (100, 7, 0), (256, 8, 1), (1000, 32, 1), (1024, 1, 0)])
+def test_topk_ties_and_edges(E, k, renorm):
+    """Selection with many exactly equal logits (ties go to the lowest expert
+    id), signed zeros, experts pushed to -inf by the bias, E not a multiple of
+    64 and the largest E and k. Logits are set exactly: token t's x is the
+    one-hot vector at position t, so logit[t, e] = w_router[e, t] + bias[e]."""
+    dev = device()
+    T = H = 128
+    rng = np.random.default_rng(E * 100 + k)
+    vals = np.array([-1.0, -0.0, 0.0, 0.5, 1.0, 2.0], np.float32)
+    wr = np.zeros((E, H), np.float32)
+    wr[:, :T] = vals[rng.integers(0, len(vals), size=(E, T))]
+    bias = np.zeros(E, np.float32)
+    bias[rng.choice(E, size=E // 4, replace=False)] = -np.inf
+    xf = np.eye(T, H, dtype=np.float32)
+    say(f"topk ties E={E} k={k} renorm={renorm}")
+    logits, idx, w = M.moe_route(to_dev_bf16(W.bf16_bits_from_f32(xf), dev), to_dev(wr, dev), to_dev(bias, dev), k,
+                                 bool(renorm))
+    lg = logits.cpu().numpy()
+    want_l = wr[:, :T].T.astype(np.float64) + bias[None, :]
+    assert np.array_equal(lg, want_l.astype(np.float32))
+    want_idx = O.oracle_topk(lg, k)
+    assert np.array_equal(idx.cpu().numpy(), want_idx)
+    want_w = O.oracle_weights(lg, want_idx, renorm)
+    assert np.allclose(w.cpu().numpy(), want_w, rtol=1e-5, atol=1e-7)
+
+
 def test_pages_top2_and_top4_shares():
     """Top-2 (0.7, 0.3) and top-4 ([0.3, 0.25, 0.25, 0.2], tie 7/15) examples:
     GPU router picks and weights, and each rank share keeps its own terms."""
