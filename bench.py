@@ -27,6 +27,13 @@ METRIC = "MoE-layer tokens/s on 1 GPU; grouped-GEMM % MFMA peak; dispatch/combin
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak
 STAGES = ["route", "dispatch", "gemm1_gate_up_swiglu", "gemm2_down", "combine"]
+# GEMM1 HBM traffic comes from rocprofv3 counter runs summarised (by
+# --summarize-counters) in this file; it is reported only while the kernel
+# sources still hash to what was profiled.
+COUNTERS_MD = os.path.join(ROOT, "profiles", "gemm1_dsr1_ep8_share_counters.md")
+GEMM1_SOURCES = ["expert_token_routing_amd/csrc/expert_ffn.hip", "expert_token_routing_amd/csrc/gemm_dma.h",
+                 "expert_token_routing_amd/csrc/gemm_tile.h", "expert_token_routing_amd/csrc/moe_device.h"]
+GEMM1_KERNEL = "grouped_gemm_dma_kernel<true>"
 
 
 def log(*a):
@@ -46,9 +53,84 @@ def parse():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB device to device once (a plain copy of "
                          "known size that scales hardware byte counters); 0 = off")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COMMAND"),
+                    help="print the markdown summary of two rocprofv3 --pmc output folders and exit")
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="extra steps timed with a 1 GiB write between them (evicts L2 / Infinity Cache); 0 = off")
     return ap.parse_args()
+
+
+def gemm1_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMM1_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_gemm1_traffic():
+    """(bytes per GEMM1 launch, note) from the committed counter summary, or
+    (None, reason) when it is missing or the kernel changed since."""
+    try:
+        with open(COUNTERS_MD) as f:
+            kv = dict(line.strip()[2:].split(": ", 1) for line in f if line.startswith("- ") and ": " in line)
+    except OSError:
+        return None, "no counter summary"
+    if kv.get("source_sha256") != gemm1_sources_sha256():
+        return None, "kernel sources changed since the counters were taken"
+    return float(kv["traffic_bytes_per_launch"]), f"rocprofv3 FETCH_SIZE/WRITE_SIZE, {os.path.basename(COUNTERS_MD)}"
+
+
+def summarize_counters(fetch_dir, write_dir, command):
+    """Markdown summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE)
+    of a bench.py run with --copy-calibration-mib: per-dispatch KiB of the
+    GEMM1 kernel, scaled by what the counters read for the calibration copy."""
+    import csv
+    import glob
+
+    def per_dispatch(d, counter):
+        out = {}
+        for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(fn)):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = int(r["Dispatch_Id"])
+                name, v = r["Kernel_Name"], float(r["Counter_Value"])
+                out[key] = (name, out.get(key, (name, 0.0))[1] + v)
+        return out
+
+    fetch, write = per_dispatch(fetch_dir, "FETCH_SIZE"), per_dispatch(write_dir, "WRITE_SIZE")
+    copy_f = max(v for n, v in fetch.values() if "copyBuffer" in n)
+    copy_w = max(v for n, v in write.values() if "copyBuffer" in n)
+    import re
+    mib = int(re.search(r"--copy-calibration-mib (\d+)", command).group(1))
+    f_scale, w_scale = mib * 1024.0 / copy_f, mib * 1024.0 / copy_w
+    g_f = [v for n, v in fetch.values() if GEMM1_KERNEL in n.replace("moe::", "").replace("void ", "")]
+    g_w = [v for n, v in write.values() if GEMM1_KERNEL in n.replace("moe::", "").replace("void ", "")]
+    f_kib, w_kib = sum(g_f) / len(g_f), sum(g_w) / len(g_w)
+    traffic = (f_kib * f_scale + w_kib * w_scale) * 1024.0
+    lines = [
+        "# HBM traffic of the gate/up GEMM (grouped_gemm_dma_kernel<true>), DeepSeek-R1-shaped share",
+        "",
+        "Two counter runs (FETCH_SIZE, then WRITE_SIZE) of the command below; the calibration copy of "
+        f"{mib} MiB device to device reads {copy_f:.0f} KiB as FETCH_SIZE and {copy_w:.0f} KiB as WRITE_SIZE, "
+        "so the counters are scaled by the factors below to bytes.",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        f"- kernel: {GEMM1_KERNEL}",
+        f"- dispatches: {len(g_f)} (FETCH_SIZE), {len(g_w)} (WRITE_SIZE)",
+        f"- fetch_kib_per_launch: {f_kib:.1f}",
+        f"- write_kib_per_launch: {w_kib:.1f}",
+        f"- fetch_scale: {f_scale:.4f}",
+        f"- write_scale: {w_scale:.4f}",
+        f"- traffic_bytes_per_launch: {traffic:.0f}",
+        f"- source_sha256: {gemm1_sources_sha256()}",
+    ]
+    return "\n".join(lines) + "\n"
 
 
 def algorithmic(cfg, N, U, fused_gather=True):
@@ -103,6 +185,9 @@ def cpu_baseline(inp, sample_tokens):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters), end="")
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU's share of the MoE layer; runs on more than one GPU are not part "
@@ -236,6 +321,7 @@ def main():
                      "note": "moe_dispatch entry point (tables + token rows copied to x_perm), timed alone"}
 
     g1 = work["gemm1_gate_up_swiglu"]["flop"] / (stage_avg[2] * 1e-3) / 1e12
+    traffic, traffic_note = recorded_gemm1_traffic() if cfg.name == "dsr1_ep8_share" else (None, "other workload")
     gemm_ms = stage_avg[2] + stage_avg[3]
     gemm_tflops = 6.0 * N * cfg.H * cfg.I / (gemm_ms * 1e-3) / 1e12
     ms_per_step = wall / args.steps * 1e3
@@ -258,7 +344,8 @@ def main():
                    "parallelism": "one EP rank's share on 1 GPU"},
         "roofline": {"bound": "mfma", "kernel": "grouped GEMM1 (gate/up + SwiGLU)",
                      "achieved": round(g1, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(g1 / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(g1 / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch", "traffic_source": traffic_note},
         "grouped_gemm": {"tflops": round(gemm_tflops, 2), "frac_mfma_bf16": round(gemm_tflops / PEAK_BF16_TFLOPS, 4)},
         "stages": stages,
         "dispatch_rows": dispatch_rows,
