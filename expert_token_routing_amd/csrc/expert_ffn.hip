@@ -14,9 +14,13 @@
 //   GEMM2:  out = h Wd
 //
 // Both are persistent kernels: every workgroup rebuilds the tile list from
-// `offsets` (m-tiles of BM rows per segment x n-tiles) and strides over it.
-// Weights are n-contiguous in memory and are transposed 8 x 8 in registers on
-// their way to LDS, so both MFMA operands are read k-contiguous from LDS.
+// `offsets` and strides over it. Two implementations:
+//  * panel_gemm_kernel (k a multiple of 32): direct global->LDS loads in
+//    64-deep stages, tiles of up to 288 rows of one expert x 256 weight
+//    columns, 16x16x32 MFMAs; the weight operand is read from LDS with
+//    transposing reads.
+//  * grouped_gemm_kernel (any k that is a multiple of 8): register-staged
+//    loads, weights transposed 8 x 8 in registers on their way to LDS.
 #include "gemm_dma.h"
 #include "gemm_tile.h"
 #include "moe_kernels.h"
@@ -152,161 +156,189 @@ grouped_gemm_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __re
   }
 }
 
-// Same computation with a deeper memory pipeline, for k a multiple of 32:
-// direct global->LDS loads into a ring of stages (three in flight while one is
-// multiplied), B read from LDS with transposing reads instead of a register
-// transpose, and the LDS reads of the next 16-deep step interleaved with the
-// MFMAs of the current one. Tiles go to XCDs in contiguous expert-major
-// ranges (workgroup b runs on XCD b % 8), so the workgroups sharing an
-// expert's weight and row panels share one L2.
-namespace dmaffn {
+// Expert-panel grouped GEMM (k a multiple of 32). A tile is a block of up to
+// 288 rows of one expert (an expert's rows are split evenly into
+// ceil(M / 288) blocks, so padding stays below 16 rows per block) x 256
+// weight columns; 8 waves as 2 wave rows x 4 wave columns of 64.
+//
+// Memory requests, not bytes, bound this kernel: every operand request is a
+// whole 128-byte line (64-deep stages: a token row's 64 k are one line), and
+// the tile shape keeps requests per output low. Stages come in through a
+// ring of two LDS buffers; stage s is read into registers during iteration
+// s - 1 and multiplied in iteration s, and its buffer is refilled with stage
+// s + 2 right after the barrier of iteration s that follows the last read.
+namespace panelffn {
 
-// One output tile: rows [r0, r0 + rows) of A (rows <= FM*64), 256 columns of
-// the expert's weight (n-tile nj). LOAD_BM rows are brought into LDS (rows past
-// the end repeat the last one); the 8 waves, 2 x 4, multiply FM*32 x 64 each.
-template <int LOAD_BM, int FM, bool SWIGLU>
-__device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __restrict__ A, int lda, int r0,
-                                         int rows, const uint16_t* __restrict__ We, int ldw, int K, int N,
-                                         int up_off, int nj, uint16_t* __restrict__ C, int ldc,
-                                         const int32_t* __restrict__ gather_src, int gather_k, int gather_rows) {
-  using namespace dma;
-  constexpr int FN = 2;
-  constexpr int kAStage = LOAD_BM * kARowBytes;
-  constexpr int kStage = kAStage + kBStageBytes;
-  constexpr int kLoads = ALoader<LOAD_BM>::kPer + BLoader::kPer;  // DMA instructions per thread per stage
-  static_assert(dma::kBK == 32, "two 16-deep steps per stage");
-  const int w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
+using namespace dma::panel;
+
+// One tile: FMT fragments per wave row (16 * kWR * FMT >= rows), `rows` rows
+// from the row source, weight columns given by col_of.
+template <int FMT, bool SWIGLU, typename SrcRow, typename ColOf>
+__device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __restrict__ Abase, int64_t a_bytes,
+                                         int lda, int rows, SrcRow src_row, const uint16_t* __restrict__ We, int ldw,
+                                         int K, ColOf col_of, int out_c0, int N, uint16_t* __restrict__ C, int ldc,
+                                         int r0) {
+  const int w = threadIdx.x >> 6, wm = w % kWR, wn = w / kWR;
   const int lane = lane_id();
-  const int nk = K / dma::kBK;
+  // stages of kSK; K is a multiple of 32, so the last stage may hold only
+  // its first k step (the second is multiplied as zeros)
+  const int nk = (K + kSK - 1) / kSK;
+  const bool half_tail = (K % kSK) != 0;
+  const int r16 = (rows + 15) & ~15;
+  MOE_LDS char* const ldsA = lds;
+  MOE_LDS char* const ldsB = lds + dma::panel::kStages * kAStage;
 
-  auto col_of = [&](int s0) -> int {
-    if (SWIGLU) {  // wave wn's 64 columns: 32 gate then the matching 32 up
-      const int q = s0 & 63;
-      const int oc = nj * 128 + (s0 >> 6) * 32 + (q & 31);
-      if (oc >= N) return 0;
-      return q < 32 ? oc : up_off + oc;
-    } else {
-      const int oc = nj * 256 + s0;
-      return oc < N ? oc : 0;
+  f32x4v acc[FMT][kFN];
+#pragma unroll
+  for (int i = 0; i < FMT; ++i)
+#pragma unroll
+    for (int j = 0; j < kFN; ++j) acc[i][j] = f32x4v{0.f, 0.f, 0.f, 0.f};
+
+  ALoaderP la;
+  la.init(Abase, a_bytes, lda, rows, r16, src_row);
+  BLoaderP lb;
+  lb.init(We, ldw, K, col_of);
+  const int nl = la.count + BLoaderP::kPer;  // DMA instructions of this wave per stage
+  auto issue = [&](int st) {
+    if (st < nk) {
+      const int buf = st % dma::panel::kStages;
+      la.issue(ldsA + buf * kAStage, st * kSK);
+      lb.issue(ldsB + buf * kBStage, st);
     }
   };
+  // Wait until stage s landed, then barrier. Stages complete in issue order;
+  // the ones issued after s (s+1 .. min(last, nk-1)) may stay in flight.
+  auto wait_stage = [&](int s, int last) {
+    const int ahead = max(0, min(last, nk - 1) - s);
+    dma::wait_vm_barrier_dyn<(dma::panel::kStages - 1) * (ALoaderP::kPerMax + BLoaderP::kPer)>(ahead * nl);
+  };
+  FragAddrP fa;
+  fa.init(wm, wn);
+  u32x4 a[FMT], b[kFN];
 
-  f32x16 acc[FM][FN];
-  zero_acc(acc);
-  ALoader<LOAD_BM> la;
-  BLoader lb;
-  if (gather_src != nullptr)  // A rows are token vectors: row r0+r is token src[r0+r] / k
-    la.init_gather(A, lda, gather_rows, rows, [&](int r) { return gather_src[r0 + r] / gather_k; });
-  else
-    la.init(A + int64_t(r0) * lda, lda, rows);
-  lb.init(We, ldw, K, col_of);
-  // ring of kStages buffers: stages kt+1 .. kt+kStages-1 in flight while
-  // stage kt is multiplied
+  for (int st = 0; st < dma::panel::kStages; ++st) issue(st);
+  wait_stage(0, dma::panel::kStages - 1);
 #pragma unroll
-  for (int p = 0; p < kStages - 1; ++p)
-    if (p < nk) {
-      la.issue(lds + p * kStage, p * dma::kBK);
-      lb.issue(lds + p * kStage + kAStage, p * dma::kBK);
-    }
-  FragAddr fa;
-  fa.init(wm * FM * 32, wn * 64);
-  Frags<FM, FN> f0, f1;
-  {  // stage 0 landed (stages 1 and 2 may be in flight)
-    const int ahead0 = min(kStages - 2, nk - 1);
-    if (ahead0 >= 2)
-      wait_vm_barrier<2 * kLoads>();
-    else if (ahead0 == 1)
-      wait_vm_barrier<kLoads>();
-    else
-      wait_vm_barrier<0>();
-  }
-  load_frags<FM, FN>(lds, lds + kAStage, fa, 0, f0);
+  for (int j = 0; j < kFN; ++j) b[j] = read_b<0>(ldsB, fa, j);
+#pragma unroll
+  for (int i = 0; i < FMT; ++i) a[i] = read_a<0>(ldsA, fa, i);
+
+  constexpr int kH1 = (FMT + 1) / 2;  // fragment rows multiplied before the barrier
   for (int kt = 0; kt < nk; ++kt) {
-    MOE_LDS char* cur = lds + (kt % kStages) * kStage;
-    // refill the buffer of stage kt-1 (every wave is past it) with stage kt+3
-    if (kt + kStages - 1 < nk) {
-      MOE_LDS char* nxt = lds + ((kt + kStages - 1) % kStages) * kStage;
-      la.issue(nxt, (kt + kStages - 1) * dma::kBK);
-      lb.issue(nxt + kAStage, (kt + kStages - 1) * dma::kBK);
+    if constexpr (kSub == 2) {
+      // k step 0 of stage kt; step 1's fragments (same buffer, landed) stream
+      // in behind it, each A row right after its last use
+      const int cb = kt % dma::panel::kStages;
+      const MOE_LDS char* cA = ldsA + cb * kAStage;
+      const MOE_LDS char* cB = ldsB + cb * kBStage;
+      u32x4 bs[kFN];
+#pragma unroll
+      for (int j = 0; j < kFN; ++j) bs[j] = read_b<1>(cB, fa, j);
+#pragma unroll
+      for (int i = 0; i < FMT; ++i) {
+#pragma unroll
+        for (int j = 0; j < kFN; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+        a[i] = read_a<1>(cA, fa, i);
+      }
+#pragma unroll
+      for (int j = 0; j < kFN; ++j) b[j] = bs[j];
+      if (half_tail && kt == nk - 1) {  // k beyond K: LDS holds other data
+#pragma unroll
+        for (int j = 0; j < kFN; ++j) b[j] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < FMT; ++i) a[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // second step's fragments stream in under the first step's MFMAs
-    load_frags<FM, FN>(cur, cur + kAStage, fa, 1, f1);
-    mma_frags<FM, FN>(f0, acc);
-    interleave_mfma_with_reads<FM, FN>();
+    // last k step of stage kt. First half: rows 0 .. kH1-1 (registers only)
+#pragma unroll
+    for (int i = 0; i < kH1; ++i)
+#pragma unroll
+      for (int j = 0; j < kFN; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < nk) {
-      // stage kt+1 landed (its successors may be in flight); all LDS reads of
-      // this wave returned before the barrier, so no buffer is refilled early
-      wait_lgkm0();
-      const int ahead = min(kStages - 2, nk - 2 - kt);
-      if (ahead >= 2)
-        wait_vm_barrier<2 * kLoads>();
-      else if (ahead == 1)
-        wait_vm_barrier<kLoads>();
-      else
-        wait_vm_barrier<0>();
+    // every wave has read stage kt (its reads were waited for), and stage
+    // kt+1 landed: refill stage kt's buffer with stage kt+kStages, read stage kt+1
+    dma::wait_lgkm0();
+    // stages issued so far: up to kt + kStages - 1
+    if (kt + 1 < nk) wait_stage(kt + 1, kt + dma::panel::kStages - 1); else dma::wait_vm_barrier<0>();
+    issue(kt + dma::panel::kStages);
+    const int nb = (kt + 1) % dma::panel::kStages;
+    const MOE_LDS char* nA = ldsA + nb * kAStage;
+    const MOE_LDS char* nB = ldsB + nb * kBStage;
+    u32x4 bn[kFN];
+#pragma unroll
+    for (int j = 0; j < kFN; ++j) bn[j] = read_b<0>(nB, fa, j);
+#pragma unroll
+    for (int i = 0; i < kH1; ++i) a[i] = read_a<0>(nA, fa, i);
+    // second half, then this stage's last A registers take the next stage's
+#pragma unroll
+    for (int i = kH1; i < FMT; ++i) {
+#pragma unroll
+      for (int j = 0; j < kFN; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+      a[i] = read_a<0>(nA, fa, i);
     }
-    // next stage's first step streams in under this stage's second step (after
-    // the last stage this reads a finished buffer; the values are not used)
-    MOE_LDS char* nx = lds + ((kt + 1) % kStages) * kStage;
-    load_frags<FM, FN>(nx, nx + kAStage, fa, 0, f0);
-    mma_frags<FM, FN>(f1, acc);
-    interleave_mfma_with_reads<FM, FN>();
+#pragma unroll
+    for (int j = 0; j < kFN; ++j) b[j] = bn[j];
     __builtin_amdgcn_sched_barrier(0);
   }
-  wait_lds_barrier();
+  dma::wait_lds_barrier();
 
+  // C: fragment (i, j) lane l -> tile row 16 (kWR i + wm) + 4 (l >> 4) + v,
+  // tile column 64 wn + 16 j + (l & 15).
   if (SWIGLU) {
+    // wave columns: 32 gate then the matching 32 up outputs
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      __builtin_amdgcn_sched_barrier(0);
-      const int col = nj * 128 + wn * 32 + (lane & 31);
+    for (int i = 0; i < FMT; ++i) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wm * FM * 32 + fm * 32 + mfma_c_row(v, lane);
-        if (row < rows && col < N) {
-          const float g = acc[fm][0][v];
-          const float u = acc[fm][1][v];
-          const float hv = g / (1.f + __expf(-g)) * u;
-          C[int64_t(r0 + row) * ldc + col] = uint16_t(f32_to_bf16_bits(hv));
+      for (int j = 0; j < 2; ++j) {
+        const int col = out_c0 + 32 * wn + 16 * j + (lane & 15);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = 16 * (kWR * i + wm) + 4 * (lane >> 4) + v;
+          if (row < rows && col < N) {
+            const float g = acc[i][j][v];
+            const float u = acc[i][j + 2][v];
+            C[int64_t(r0 + row) * ldc + col] = uint16_t(f32_to_bf16_bits(g / (1.f + __expf(-g)) * u));
+          }
         }
       }
     }
   } else {
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int i = 0; i < FMT; ++i)
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        __builtin_amdgcn_sched_barrier(0);
-        const int col = nj * 256 + wn * 64 + fn * 32 + (lane & 31);
+      for (int j = 0; j < kFN; ++j) {
+        const int col = out_c0 + 64 * wn + 16 * j + (lane & 15);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = wm * FM * 32 + fm * 32 + mfma_c_row(v, lane);
-          if (row < rows && col < N) C[int64_t(r0 + row) * ldc + col] = uint16_t(f32_to_bf16_bits(acc[fm][fn][v]));
+        for (int v = 0; v < 4; ++v) {
+          const int row = 16 * (kWR * i + wm) + 4 * (lane >> 4) + v;
+          if (row < rows && col < N) C[int64_t(r0 + row) * ldc + col] = uint16_t(f32_to_bf16_bits(acc[i][j][v]));
         }
       }
   }
 }
 
-}  // namespace dmaffn
+}  // namespace panelffn
 
+// Tiles: expert i has nrt_i = ceil(M_i / 288) row blocks of equal height (a
+// multiple of 16) times ntn column tiles, ordered expert-major, column-major
+// inside the expert (the row blocks sharing a weight panel are adjacent and
+// run together); each XCD takes a contiguous range, dealt round robin to its
+// workgroups (workgroup b runs on XCD b % 8).
 template <bool SWIGLU>
 __global__ void __launch_bounds__(dma::kThreads)
-grouped_gemm_dma_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __restrict__ offsets, int E_local,
-                        int64_t capacity, const uint16_t* __restrict__ W, int64_t w_expert_stride, int ldw,
-                        uint16_t* __restrict__ C, int ldc, int K, int N, int up_off,
-                        const int32_t* __restrict__ gather_src, int gather_k, int gather_rows) {
-  using namespace dma;
-  __shared__ __attribute__((aligned(1024))) char smem[kStages * (256 * kARowBytes + kBStageBytes)];
+panel_gemm_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __restrict__ offsets, int E_local,
+                  int64_t capacity, const uint16_t* __restrict__ W, int64_t w_expert_stride, int ldw,
+                  uint16_t* __restrict__ C, int ldc, int K, int N, int up_off, const int32_t* __restrict__ gather_src,
+                  int gather_k, int gather_rows) {
+  using namespace dma::panel;
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   __shared__ int s_off[kMaxLocal + 1];
   __shared__ int s_tpre[kMaxLocal + 1];
-  __shared__ int s_tmp[kWaves];
+  __shared__ int s_tmp[dma::kWaves];
   MOE_LDS char* lds = (MOE_LDS char*)smem;
 
-  const int ntn = SWIGLU ? (N + 127) / 128 : (N + 255) / 256;
-  // Tiles of expert i: ceil(M_i / 256) row tiles x ntn n-tiles, ordered
-  // n-major so that the row tiles sharing one weight panel are adjacent (and
-  // run together).
+  const int ntn = SWIGLU ? (N + kBN / 2 - 1) / (kBN / 2) : (N + kBN - 1) / kBN;
   constexpr int kPerT = (kMaxLocal + dma::kThreads - 1) / dma::kThreads;
   int mt[kPerT];
   int sum = 0;
@@ -318,7 +350,7 @@ grouped_gemm_dma_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* 
       const int64_t a = min<int64_t>(max<int64_t>(offsets[i], 0), capacity);
       const int64_t b = max<int64_t>(a, min<int64_t>(offsets[i + 1], capacity));
       s_off[i] = int(a);
-      mt[q] = int((b - a + 255) / 256) * ntn;
+      mt[q] = int((b - a + kRowsMax - 1) / kRowsMax) * ntn;
       if (i == E_local - 1) s_off[E_local] = int(b);
     }
     sum += mt[q];
@@ -334,9 +366,6 @@ grouped_gemm_dma_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* 
   if (threadIdx.x == 0) s_tpre[E_local] = total;
   __syncthreads();
 
-  // This XCD's contiguous range of the tile list, dealt round robin to its
-  // workgroups: tiles of equal cost keep the workgroups in step, so the tiles
-  // sharing a panel stream it through the XCD's L2 together.
   const int nxcd = 8;
   const int xcd = blockIdx.x % nxcd;
   const int per_xcd = gridDim.x / nxcd;
@@ -351,18 +380,54 @@ grouped_gemm_dma_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* 
       else
         hi = mid - 1;
     }
-    // per-tile values are uniform across the workgroup
     const int e = __builtin_amdgcn_readfirstlane(lo);
     const int t0 = __builtin_amdgcn_readfirstlane(s_tpre[e]);
-    const int local = tile - t0;
-    const int mte = (__builtin_amdgcn_readfirstlane(s_tpre[e + 1]) - t0) / ntn;
-    const int nj = local / mte;
-    const int mi = local - nj * mte;
     const int seg0 = __builtin_amdgcn_readfirstlane(s_off[e]);
-    const int r0 = seg0 + mi * 256;
-    const int rows = min(256, __builtin_amdgcn_readfirstlane(s_off[e + 1]) - r0);
-    dmaffn::run_tile<256, 4, SWIGLU>(lds, A, lda, r0, rows, W + int64_t(e) * w_expert_stride, ldw, K, N, up_off, nj,
-                                      C, ldc, gather_src, gather_k, gather_rows);
+    const int m_e = __builtin_amdgcn_readfirstlane(s_off[e + 1]) - seg0;
+    const int nrt = (m_e + kRowsMax - 1) / kRowsMax;
+    const int local = tile - t0;
+    const int nj = local / nrt;
+    const int mi = local - nj * nrt;
+    const int height = ((m_e + nrt - 1) / nrt + 15) & ~15;
+    const int r0 = seg0 + mi * height;
+    const int rows = min(height, seg0 + m_e - r0);
+    if (rows <= 0) continue;
+    const uint16_t* We = W + int64_t(e) * w_expert_stride;
+    auto col_of = [&](int s0) -> int {
+      if (SWIGLU) {  // tile column s: wave column s/64, gate (s%64 < 32) or up of output o0 + 32*(s/64) + s%32
+        const int q = s0 & 63;
+        const int oc = nj * (kBN / 2) + (s0 >> 6) * 32 + (q & 31);
+        if (oc >= N) return 0;
+        return q < 32 ? oc : up_off + oc;
+      } else {
+        const int oc = nj * kBN + s0;
+        return oc < N ? oc : 0;
+      }
+    };
+    const int out_c0 = SWIGLU ? nj * (kBN / 2) : nj * kBN;
+    const int fmt = (rows + 16 * kWR - 1) / (16 * kWR);
+    auto go = [&](auto fm_t) {
+      constexpr int FMT = decltype(fm_t)::value;
+      if (gather_src != nullptr) {
+        panelffn::run_tile<FMT, SWIGLU>(lds, A, int64_t(gather_rows) * lda * 2, lda, rows,
+                                        [&](int r) { return gather_src[r0 + r] / gather_k; }, We, ldw, K, col_of,
+                                        out_c0, N, C, ldc, r0);
+      } else {
+        panelffn::run_tile<FMT, SWIGLU>(lds, A + int64_t(r0) * lda, int64_t(rows) * lda * 2, lda, rows,
+                                        [](int r) { return r; }, We, ldw, K, col_of, out_c0, N, C, ldc, r0);
+      }
+    };
+    switch (fmt) {
+      case 1: go(std::integral_constant<int, 1>{}); break;
+      case 2: go(std::integral_constant<int, 2>{}); break;
+      case 3: go(std::integral_constant<int, 3>{}); break;
+      case 4: go(std::integral_constant<int, 4>{}); break;
+      case 5: go(std::integral_constant<int, 5>{}); break;
+      case 6: go(std::integral_constant<int, 6>{}); break;
+      case 7: go(std::integral_constant<int, 7>{}); break;
+      case 8: go(std::integral_constant<int, 8>{}); break;
+      default: go(std::integral_constant<int, 9>{}); break;
+    }
   }
 }
 
@@ -383,10 +448,9 @@ unsigned dma_grid(int64_t tiles) {
 hipError_t launch_expert_gemm1(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_gate_up, int H,
                                int I, int E_local, int64_t capacity, uint16_t* h, hipStream_t stream) {
   if (H % dma::kBK == 0) {
-    const int64_t tiles = (ceil_div(capacity, 256) + 2 * E_local) * ceil_div(I, 128);
-    hipLaunchKernelGGL((grouped_gemm_dma_kernel<true>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream,
-                       x_perm, H, offsets, E_local, capacity, w_gate_up, int64_t(H) * 2 * I, 2 * I, h, I, H, I, I,
-                       nullptr, 1, 0);
+    const int64_t tiles = (ceil_div(capacity, dma::panel::kRowsMax) + E_local) * ceil_div(I, dma::panel::kBN / 2);
+    hipLaunchKernelGGL((panel_gemm_kernel<true>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream, x_perm, H,
+                       offsets, E_local, capacity, w_gate_up, int64_t(H) * 2 * I, 2 * I, h, I, H, I, I, nullptr, 1, 0);
     return hipGetLastError();
   }
   const int64_t mt_bound = ceil_div(capacity, kFfnBM) + E_local;
@@ -399,10 +463,9 @@ hipError_t launch_expert_gemm1(const uint16_t* x_perm, const int32_t* offsets, c
 hipError_t launch_expert_gemm2(const uint16_t* h, const int32_t* offsets, const uint16_t* w_down, int H, int I,
                                int E_local, int64_t capacity, uint16_t* out, hipStream_t stream) {
   if (I % dma::kBK == 0) {
-    const int64_t tiles = (ceil_div(capacity, 256) + 2 * E_local) * ceil_div(H, 256);
-    hipLaunchKernelGGL((grouped_gemm_dma_kernel<false>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0,
-                       stream, h, I, offsets, E_local, capacity, w_down, int64_t(I) * H, H, out, H, I, H, 0, nullptr, 1,
-                       0);
+    const int64_t tiles = (ceil_div(capacity, dma::panel::kRowsMax) + E_local) * ceil_div(H, dma::panel::kBN);
+    hipLaunchKernelGGL((panel_gemm_kernel<false>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream, h, I,
+                       offsets, E_local, capacity, w_down, int64_t(I) * H, H, out, H, I, H, 0, nullptr, 1, 0);
     return hipGetLastError();
   }
   const int64_t mt_bound = ceil_div(capacity, kFfnBM) + E_local;
@@ -417,9 +480,9 @@ bool expert_gemm1_can_gather(int T, int H) { return H % dma::kBK == 0 && int64_t
 hipError_t launch_expert_gemm1_gather(const uint16_t* x, const int32_t* perm_src, int T, int k, const int32_t* offsets,
                                       const uint16_t* w_gate_up, int H, int I, int E_local, int64_t capacity,
                                       uint16_t* h, hipStream_t stream) {
-  const int64_t tiles = (ceil_div(capacity, 256) + 2 * E_local) * ceil_div(I, 128);
-  hipLaunchKernelGGL((grouped_gemm_dma_kernel<true>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream, x, H,
-                     offsets, E_local, capacity, w_gate_up, int64_t(H) * 2 * I, 2 * I, h, I, H, I, I, perm_src, k, T);
+  const int64_t tiles = (ceil_div(capacity, dma::panel::kRowsMax) + E_local) * ceil_div(I, dma::panel::kBN / 2);
+  hipLaunchKernelGGL((panel_gemm_kernel<true>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream, x, H, offsets,
+                     E_local, capacity, w_gate_up, int64_t(H) * 2 * I, 2 * I, h, I, H, I, I, perm_src, k, T);
   return hipGetLastError();
 }
 

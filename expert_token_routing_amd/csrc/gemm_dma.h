@@ -1,22 +1,20 @@
 // Matrix-core tile pieces fed by direct global->LDS loads (gfx950).
 //
-// A workgroup of 512 threads (8 waves, 2 x 4) computes a BM x 256 output tile
-// in k stages of 32. Each stage is brought into LDS by 16-byte
-// buffer_load_dwordx4 ... lds: lane l of a wave writes LDS bytes
-// [base + 16 l, base + 16 l + 16), so the per-lane global offset picks the
-// LDS layout. A ring of kStages stages keeps kStages - 1 of them in flight
-// while one is multiplied, enough bytes to cover the HBM latency.
+// Operands are brought into LDS by 16-byte buffer_load_dwordx4 ... lds: lane l
+// of a wave writes LDS bytes [base + 16 l, base + 16 l + 16), so the per-lane
+// global offset picks the LDS layout. Completion is tracked with s_waitcnt
+// vmcnt per wave plus a workgroup barrier.
 //
-// LDS layouts (both conflict-free on the 64 banks of 4 bytes of gfx950):
-//  * A (k-contiguous rows): row r occupies bytes [64 r, 64 r + 64); its
-//    16-byte chunk c (k = 8c .. 8c+7) sits at chunk position c ^ ((r >> 2) & 3),
-//    so 16 lanes reading one chunk of 16 consecutive rows (ds_read_b128) hit 16
-//    different 16-byte slots of a 256-byte bank window.
-//  * B (n-contiguous, [k][n] as in memory): 4 x 16 blocks of 128 bytes, block
-//    (kq, nq) = rows 4kq .. 4kq+3, columns 16nq .. 16nq+15, at byte
-//    128 (kq * BN/16 + nq), row r of the block at +32 r. ds_read_b64_tr_b16
-//    reads one block per group of 16 lanes and hands lane i the 4 k-values of
-//    column i; two such reads give the 8 k-values of an MFMA B fragment.
+// LDS layouts (conflict-free on the 64 banks of 4 bytes of gfx950):
+//  * k-contiguous rows (token rows, router weight planes): row r holds the
+//    stage's k range contiguously; its 16-byte chunks are XOR-swizzled with
+//    row bits so that 16 lanes reading one chunk of 16 consecutive rows
+//    (ds_read_b128) hit 16 different 16-byte slots of a 256-byte bank window.
+//  * n-contiguous weights ([k][n] as in memory): 4 x 16 blocks of 128 bytes,
+//    block (kq, nq) = rows 4kq .. 4kq+3, columns 16nq .. 16nq+15, row r of
+//    the block at +32 r. ds_read_b64_tr_b16 reads one block per group of 16
+//    lanes and hands lane i the 4 k-values of column i; two such reads give
+//    the 8 k-values of an MFMA B fragment.
 #pragma once
 
 #include "moe_device.h"
@@ -24,13 +22,10 @@
 namespace moe {
 namespace dma {
 
-constexpr int kBK = 32;
-constexpr int kStages = 4;
+constexpr int kBK = 32;                       // k per stage of the router pipeline
+constexpr int kStages = 4;                    // router pipeline depth
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kBN = 256;
-constexpr int kNQ = kBN / 16;                 // 16-column blocks per B stage
-constexpr int kBStageBytes = kBK * kBN * 2;   // 16 KiB
 constexpr int kARowBytes = kBK * 2;           // 64
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -45,6 +40,19 @@ __device__ __forceinline__ void wait_vm_barrier() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
+}
+// wait_vm_barrier<n> for a wave-uniform n known only at run time; n above
+// MAX waits for MAX (stricter, never looser).
+template <int MAX>
+__device__ __forceinline__ void wait_vm_barrier_dyn(int n) {
+  if constexpr (MAX == 0) {
+    wait_vm_barrier<0>();
+  } else {
+    if (n >= MAX)
+      wait_vm_barrier<MAX>();
+    else
+      wait_vm_barrier_dyn<MAX - 1>(n);
+  }
 }
 // All LDS reads of this wave returned (vmcnt / expcnt left alone).
 __device__ __forceinline__ void wait_lgkm0() {
@@ -130,102 +138,146 @@ struct ALoader {
   }
 };
 
-// B stage: 32 k x 256 n of an n-contiguous matrix (leading dimension ldw).
-// Wave w issues 2 loads; load j fills blocks 8 (j*8 + w) .. +7 (kq = block / 16).
-// col_of(s) maps tile column s (a multiple of 8) to a valid matrix column.
-struct BLoader {
-  static constexpr int kPer = kBK / 4 * kNQ / 8 / kWaves;  // 2
+// ---------------------------------------------------------------------------
+// Expert-panel tiles: a block of up to kRowsMax rows of one expert (its rows
+// split evenly over ceil(rows / kRowsMax) blocks) x kBN weight columns.
+// v_mfma_f32_16x16x32_bf16:
+//   A fragment: lane l holds A[l % 16][8*(l/16) .. +7]
+//   B fragment: lane l holds B[8*(l/16) .. +7][l % 16]
+//   C: lane l holds column l % 16, rows 4*(l/16) .. +3
+// 8 waves: kWR wave rows x kWC wave columns of 64. 16-row fragment f of the
+// tile belongs to wave row f % kWR (as its fragment f / kWR), so any row count
+// splits over the wave rows to within one fragment.
+// ---------------------------------------------------------------------------
+namespace panel {
+
+constexpr int kWR = 2;                       // wave rows (kWaves / kWR wave columns of 64)
+constexpr int kWC = kWaves / kWR;
+constexpr int kBN = 64 * kWC;                // weight columns per tile
+constexpr int kFMMax = 9;                    // 16-row fragments per wave row
+constexpr int kRowsMax = 16 * kFMMax * kWR;  // rows per tile
+constexpr int kFN = 4;                       // 16-column fragments per wave
+constexpr int kNQ = kBN / 16;                // 16-column blocks of a B stage
+constexpr int kSK = 64;                      // k per LDS stage (32 or 64)
+constexpr int kSub = kSK / 32;               // MFMA k steps per stage
+constexpr int kRowBytes = kSK * 2;           // bytes of one A row in a stage (64 or 128)
+constexpr int kLanesPerRow = kRowBytes / 16; // 4 or 8
+constexpr int kRowsPerLoad = 64 / kLanesPerRow;
+constexpr int kAStage = kRowsMax * kRowBytes;
+constexpr int kBStage = kSK * kBN * 2;
+constexpr int kStages = (160 * 1024 - 2048) / (kAStage + kBStage) >= 4 ? 4 : (160 * 1024 - 2048) / (kAStage + kBStage);
+constexpr int kLdsBytes = kStages * (kAStage + kBStage);
+static_assert(kStages >= 2, "two stages must fit in LDS");
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4v mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4v& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+// Position of 16-byte chunk c of row r inside the row: rows are kRowBytes
+// long, so a 256-byte bank window holds 256 / kRowBytes rows; the swizzle
+// makes the 16 rows read by a 16-lane ds_read_b128 phase (same chunk) land on
+// 16 different 16-byte slots.
+__device__ __forceinline__ int a_chunk_pos(int r, int c) {
+  return kSK == 32 ? (c ^ ((r >> 2) & 3)) : (c ^ ((r >> 1) & 7));
+}
+
+// A stage: R16 rows (a multiple of 16) x kSK k. Load j (kRowsPerLoad rows,
+// kLanesPerRow lanes per row) is issued by wave j % 8; wave w issues
+// count(w) of them, at most kPerMax.
+struct ALoaderP {
+  static constexpr int kPerMax = (kRowsMax / kRowsPerLoad + kWaves - 1) / kWaves;
+  i32x4 rsrc;
+  uint32_t voff[kPerMax];
+  int count;
+  template <typename SrcRow>
+  __device__ __forceinline__ void init(const uint16_t* base, int64_t bytes, int lda, int rows, int r16,
+                                       SrcRow src_row) {
+    rsrc = buffer_rsrc(base, bytes);
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nloads = r16 / kRowsPerLoad;
+    count = __builtin_amdgcn_readfirstlane(max(0, (nloads - w + kWaves - 1) / kWaves));
+#pragma unroll
+    for (int i = 0; i < kPerMax; ++i) {
+      const int r = kRowsPerLoad * (i * kWaves + w) + lane / kLanesPerRow;
+      const int c = a_chunk_pos(r, lane % kLanesPerRow);
+      voff[i] = uint32_t(src_row(min(r, rows - 1))) * uint32_t(lda) * 2u + 16u * uint32_t(c);
+    }
+  }
+  __device__ __forceinline__ void issue(MOE_LDS char* As, int k0) const {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int i = 0; i < kPerMax; ++i)
+      if (i < count) dma16(rsrc, voff[i], 2u * uint32_t(k0), As + 1024 * (i * kWaves + w));
+  }
+};
+
+// B stage: kSK k x kBN columns of an n-contiguous matrix, 4 x 16 blocks of
+// 128 bytes at 128 (kq * kNQ + nq); load j of wave w fills blocks
+// 8 (j * 8 + w) .. +7.
+struct BLoaderP {
+  static constexpr int kPer = kSK / 4 * kNQ / 8 / kWaves;
   i32x4 rsrc;
   uint32_t voff[kPer];
   uint32_t stage_bytes;
   template <typename ColOf>
   __device__ __forceinline__ void init(const uint16_t* W, int ldw, int K, ColOf col_of) {
     rsrc = buffer_rsrc(W, int64_t(K) * ldw * 2);
-    stage_bytes = uint32_t(ldw) * 2u;
+    stage_bytes = uint32_t(ldw) * 2u * kSK;
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int blk = 8 * (j * kWaves + w) + (lane >> 3);
-      const int kq = blk / kNQ;
-      const int nq = blk % kNQ;
-      const int r = (lane & 7) >> 1;
-      const int c = lane & 1;
+      const int kq = blk / kNQ, nq = blk % kNQ;
+      const int r = (lane & 7) >> 1, c = lane & 1;
       voff[j] = uint32_t(4 * kq + r) * uint32_t(ldw) * 2u + 2u * uint32_t(col_of(16 * nq + 8 * c));
     }
   }
-  __device__ __forceinline__ void issue(MOE_LDS char* Bs, int k0) const {
-    const int w = threadIdx.x >> 6;
+  __device__ __forceinline__ void issue(MOE_LDS char* Bs, int stage) const {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) dma16(rsrc, voff[j], uint32_t(k0) * stage_bytes, Bs + 8 * (j * kWaves + w) * 128);
+    for (int j = 0; j < kPer; ++j) dma16(rsrc, voff[j], uint32_t(stage) * stage_bytes, Bs + 1024 * (j * kWaves + w));
   }
 };
 
-// Per-lane LDS byte offsets of this wave's MFMA fragments inside one stage.
-// A: row m = wrow0 + fm*32 + (lane & 31) at 64 m (+ 2048 fm as an
-//    immediate), chunk (2 ks + lane/32) ^ ((m >> 2) & 3): one base per ks.
-// B: block (kq, nq) with kq = 4 ks + 2 (lane/32) (+1 for the upper four k),
-//    nq = wcol0/16 + 2 fn + ((lane >> 4) & 1): one base, the rest immediates.
-struct FragAddr {
-  uint32_t a[kBK / 16];
+// Per-lane LDS offsets of one wave's fragments in a stage.
+// A: fragment i of wave row wm covers tile rows 16 (kWR i + wm) .. +15; lane l
+//    reads row 16 (kWR i + wm) + (l & 15), chunk 4 q + (l >> 4) of k step q
+//    (swizzled; the swizzle depends on row bits that fragment i does not
+//    change), so one base per k step plus 16 kWR kRowBytes i.
+// B: fragment j = columns 64 wn + 16 j; lane group g = l >> 4 takes k
+//    32 q + 8g .. +7 from blocks (8 q + 2g, nq) and (8 q + 2g + 1, nq).
+struct FragAddrP {
+  uint32_t a[kSub];
   uint32_t b;
-  __device__ __forceinline__ void init(int wrow0, int wcol0) {
+  __device__ __forceinline__ void init(int wm, int wn) {
     const int lane = lane_id();
-    const int m = wrow0 + (lane & 31);
-    const int sw = (m >> 2) & 3;
-    const int khalf = lane >> 5;
+    const int r = 16 * wm + (lane & 15);
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) a[ks] = uint32_t(m * kARowBytes + 16 * ((2 * ks + khalf) ^ sw));
-    b = uint32_t((2 * khalf * kNQ + wcol0 / 16 + ((lane >> 4) & 1)) * 128 + 8 * (lane & 15));
+    for (int q = 0; q < kSub; ++q) a[q] = uint32_t(r * kRowBytes + 16 * a_chunk_pos(r, 4 * q + (lane >> 4)));
+    b = uint32_t((2 * (lane >> 4) * kNQ + 4 * wn) * 128 + 8 * (lane & 15));
   }
 };
 
-template <int FM, int FN>
-struct Frags {
-  u32x4 a[FM];
-  u32x4 b[FN];
-};
-
-// Issue the LDS reads of one 16-deep step's fragments (FM b128 + 2 FN tr reads).
-template <int FM, int FN>
-__device__ __forceinline__ void load_frags(const MOE_LDS char* As, const MOE_LDS char* Bs, const FragAddr& fa, int ks,
-                                           Frags<FM, FN>& f) {
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
-    f.a[fm] = *reinterpret_cast<const MOE_LDS u32x4*>(As + fa.a[ks] + fm * 32 * kARowBytes);
-#pragma unroll
-  for (int fn = 0; fn < FN; ++fn) {
-    const MOE_LDS char* p0 = Bs + fa.b + ks * (4 * kNQ * 128) + fn * 256;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4*)(p0));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4*)(p0 + kNQ * 128));
-    const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-    const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-    f.b[fn] = u32x4{l2.x, l2.y, h2.x, h2.y};
-  }
+template <int Q>
+__device__ __forceinline__ u32x4 read_a(const MOE_LDS char* As, const FragAddrP& fa, int i) {
+  return *reinterpret_cast<const MOE_LDS u32x4*>(As + fa.a[Q] + 16 * kWR * kRowBytes * i);
+}
+template <int Q>
+__device__ __forceinline__ u32x4 read_b(const MOE_LDS char* Bs, const FragAddrP& fa, int j) {
+  const MOE_LDS char* p0 = Bs + fa.b + Q * 8 * kNQ * 128 + 128 * j;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4*)(p0));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4*)(p0 + kNQ * 128));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+  const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2.x, l2.y, h2.x, h2.y};
 }
 
-template <int FM, int FN>
-__device__ __forceinline__ void mma_frags(const Frags<FM, FN>& f, f32x16 (&acc)[FM][FN]) {
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma32x32x16(f.a[fm], f.b[fn], acc[fm][fn]);
-}
-
-// Ask the scheduler to alternate the region's MFMAs with its LDS reads, so
-// the reads of the next step stream in under the current step's MFMAs.
-template <int FM, int FN>
-__device__ __forceinline__ void interleave_mfma_with_reads() {
-  constexpr int kMfma = FM * FN;
-  constexpr int kReads = FM + 2 * FN;
-#pragma unroll
-  for (int i = 0; i < kMfma; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    if (i < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-  }
-#pragma unroll
-  for (int i = kMfma; i < kReads; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-}
+}  // namespace panel
 
 }  // namespace dma
 }  // namespace moe

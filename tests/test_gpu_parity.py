@@ -49,11 +49,13 @@ SMALL_CASES = [
     ragged("ragged_c", T=129, H=72, I=24, E=7, k=7, e0=6, E_local=1),
     ragged("single_token", T=1, H=64, I=64, E=9, k=2, e0=0, E_local=9),
     ragged("many_experts", T=257, H=136, I=72, E=1024, k=32, e0=512, E_local=96),
-    # k extents multiples of 64 (the direct-to-LDS GEMM path) with ragged n
-    # tails and several m-tiles per expert
+    # k extents multiples of 32 (the direct-to-LDS GEMM path) with ragged n
+    # tails and several row blocks per expert
     ragged("dma_ragged_n", T=300, H=192, I=320, E=12, k=3, e0=4, E_local=5),
     ragged("dma_multi_mtile", T=1500, H=256, I=384, E=4, k=2, e0=0, E_local=4),
     ragged("dma_wide_n", T=640, H=576, I=448, E=16, k=4, e0=3, E_local=6, renormalize=0),
+    # k extents that end in half a 64-deep stage (H % 64 == I % 64 == 32)
+    ragged("dma_half_stage", T=700, H=160, I=224, E=8, k=2, e0=2, E_local=4),
 ]
 
 
