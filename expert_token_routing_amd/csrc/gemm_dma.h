@@ -138,6 +138,33 @@ struct ALoader {
   }
 };
 
+// ROWS k-contiguous rows x 64 k (128 bytes per row, one whole line per
+// request). Row r occupies LDS bytes [128 r, 128 r + 128); its chunk c
+// (k = 8c .. 8c+7) sits at position c ^ ((r >> 1) & 7). Load i of wave w
+// fills rows 8 (i * kWaves + w) .. +7, 8 lanes per row.
+template <int ROWS>
+struct RowLoader64 {
+  static constexpr int kPer = ROWS / 8 / kWaves;
+  i32x4 rsrc;
+  uint32_t voff[kPer];
+  __device__ __forceinline__ void init(const uint16_t* tile_base, int ld, int rows) {
+    rsrc = buffer_rsrc(tile_base, int64_t(rows) * ld * 2);
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int r = 8 * (i * kWaves + w) + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      voff[i] = uint32_t(min(r, rows - 1)) * uint32_t(ld) * 2u + 16u * uint32_t(c);
+    }
+  }
+  __device__ __forceinline__ void issue(MOE_LDS char* dst, int k0) const {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) dma16(rsrc, voff[i], 2u * uint32_t(k0), dst + 1024 * (i * kWaves + w));
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Expert-panel tiles: a block of up to kRowsMax rows of one expert (its rows
 // split evenly over ceil(rows / kRowsMax) blocks) x kBN weight columns.

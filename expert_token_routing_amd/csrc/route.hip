@@ -103,49 +103,54 @@ route_logits_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
     }
 }
 
-// Same logits through the direct-to-LDS pipeline (H a multiple of 32): tiles
-// of 128 tokens x 128 experts, 8 waves of 64 x 32, a ring of four 32-deep
-// stages holding the token rows and the three weight planes, all k-contiguous
-// rows in the swizzled layout.
+// Same logits through the direct-to-LDS pipeline (H a multiple of 64): tiles
+// of 128 tokens x 128 experts, 8 waves of 64 x 32. The token rows and the
+// three weight planes come in 64-deep stages (every request a whole 128-byte
+// line) through two LDS buffers; stage s + 2 is issued right after the
+// barrier at which every wave has finished reading stage s.
 namespace routedma {
 
 constexpr int kBM = 128, kBN = 128, kFM = 2, kPlanes = 3;
-constexpr int kRowStage = 128 * dma::kARowBytes;                  // 8 KiB per 128-row operand
+constexpr int kSK = 64;                                            // k per stage
+constexpr int kRowStage = 128 * kSK * 2;                           // 16 KiB per 128-row operand
 constexpr int kStage = kRowStage * (1 + kPlanes);                  // tokens + 3 planes
-constexpr int kLoads = (1 + kPlanes) * dma::ALoader<128>::kPer;    // DMA instructions per thread per stage
+constexpr int kBufs = 2;
 
 __global__ void __launch_bounds__(dma::kThreads)
 route_logits_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes,
                         const float* __restrict__ bias, float* __restrict__ logits, int T, int H, int E) {
   using namespace dma;
-  __shared__ __attribute__((aligned(1024))) char smem[kStages * kStage];
+  __shared__ __attribute__((aligned(1024))) char smem[kBufs * kStage];
   MOE_LDS char* lds = (MOE_LDS char*)smem;
   const int t0 = blockIdx.x * kBM;
   const int n0 = blockIdx.y * kBN;
   const int w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
   const int lane = lane_id();
-  const int nk = H / dma::kBK;
+  const int nk = H / kSK;
   const int64_t plane = int64_t(E) * H;
 
-  ALoader<128> la, lb[kPlanes];
+  RowLoader64<128> la, lb[kPlanes];
   la.init(x + int64_t(t0) * H, H, min(kBM, T - t0));
 #pragma unroll
   for (int p = 0; p < kPlanes; ++p) lb[p].init(planes + p * plane + int64_t(n0) * H, H, min(kBN, E - n0));
-  auto issue = [&](MOE_LDS char* st, int k0) {
-    la.issue(st, k0);
+  auto issue = [&](int st) {
+    if (st < nk) {
+      MOE_LDS char* dst = lds + (st % kBufs) * kStage;
+      la.issue(dst, st * kSK);
 #pragma unroll
-    for (int p = 0; p < kPlanes; ++p) lb[p].issue(st + (1 + p) * kRowStage, k0);
+      for (int p = 0; p < kPlanes; ++p) lb[p].issue(dst + (1 + p) * kRowStage, st * kSK);
+    }
   };
-  // fragment offsets: A rows wm*64 + fm*32 + lane%32, B rows wn*32 + lane%32,
-  // both in the swizzled k-contiguous row layout
+  // fragment offsets of 16-deep step ks (0..3): A rows wm*64 + fm*32 + lane%32,
+  // B rows wn*32 + lane%32, chunk 2 ks + lane/32, swizzled as RowLoader64
   const int khalf = lane >> 5;
   const int ma = wm * 64 + (lane & 31);
   const int mb = wn * 32 + (lane & 31);
-  uint32_t aoff[2], boff[2];
+  uint32_t aoff[kSK / 16], boff[kSK / 16];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    aoff[ks] = uint32_t(ma * kARowBytes + 16 * ((2 * ks + khalf) ^ ((ma >> 2) & 3)));
-    boff[ks] = uint32_t(mb * kARowBytes + 16 * ((2 * ks + khalf) ^ ((mb >> 2) & 3)));
+  for (int ks = 0; ks < kSK / 16; ++ks) {
+    aoff[ks] = uint32_t(ma * 128 + 16 * ((2 * ks + khalf) ^ ((ma >> 1) & 7)));
+    boff[ks] = uint32_t(mb * 128 + 16 * ((2 * ks + khalf) ^ ((mb >> 1) & 7)));
   }
   struct F {
     u32x4 a[kFM];
@@ -154,7 +159,7 @@ route_logits_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
   auto load = [&](const MOE_LDS char* st, int ks, F& f) {
 #pragma unroll
     for (int fm = 0; fm < kFM; ++fm)
-      f.a[fm] = *reinterpret_cast<const MOE_LDS u32x4*>(st + aoff[ks] + fm * 32 * kARowBytes);
+      f.a[fm] = *reinterpret_cast<const MOE_LDS u32x4*>(st + aoff[ks] + fm * 32 * 128);
 #pragma unroll
     for (int p = 0; p < kPlanes; ++p)
       f.b[p] = *reinterpret_cast<const MOE_LDS u32x4*>(st + (1 + p) * kRowStage + boff[ks]);
@@ -177,40 +182,37 @@ route_logits_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
       if (i < kFM + kPlanes) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
+  constexpr int kLoads = (1 + kPlanes) * RowLoader64<128>::kPer;  // DMA instructions per wave per stage
 
-#pragma unroll
-  for (int p = 0; p < kStages - 1; ++p)
-    if (p < nk) issue(lds + p * kStage, p * dma::kBK);
-  {
-    const int ahead0 = min(kStages - 2, nk - 1);
-    if (ahead0 >= 2)
-      wait_vm_barrier<2 * kLoads>();
-    else if (ahead0 == 1)
-      wait_vm_barrier<kLoads>();
-    else
-      wait_vm_barrier<0>();
-  }
+  issue(0);
+  issue(1);
+  if (nk > 1)
+    wait_vm_barrier<kLoads>();
+  else
+    wait_vm_barrier<0>();
   F f0, f1;
   load(lds, 0, f0);
   for (int kt = 0; kt < nk; ++kt) {
-    MOE_LDS char* cur = lds + (kt % kStages) * kStage;
-    if (kt + kStages - 1 < nk) issue(lds + ((kt + kStages - 1) % kStages) * kStage, (kt + kStages - 1) * dma::kBK);
+    const MOE_LDS char* cur = lds + (kt % kBufs) * kStage;
+    // steps 0..2: each step's MFMAs cover the next step's LDS reads
     load(cur, 1, f1);
     mma(f0);
     interleave();
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < nk) {
-      wait_lgkm0();
-      const int ahead = min(kStages - 2, nk - 2 - kt);
-      if (ahead >= 2)
-        wait_vm_barrier<2 * kLoads>();
-      else if (ahead == 1)
-        wait_vm_barrier<kLoads>();
-      else
-        wait_vm_barrier<0>();
-    }
-    MOE_LDS char* nx = lds + ((kt + 1) % kStages) * kStage;
-    load(nx, 0, f0);
+    load(cur, 2, f0);
+    mma(f1);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    load(cur, 3, f1);
+    mma(f0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    // step 3: every wave is done reading stage kt and stage kt+1 (the only
+    // one in flight) landed; refill this buffer with stage kt+2
+    wait_lgkm0();
+    wait_vm_barrier<0>();
+    issue(kt + 2);
+    load(lds + ((kt + 1) % kBufs) * kStage, 0, f0);  // stage nk: a finished buffer, values unused
     mma(f1);
     interleave();
     __builtin_amdgcn_sched_barrier(0);
@@ -313,7 +315,7 @@ hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b
   }
   {
     dim3 grid(unsigned((T + 127) / 128), unsigned((E + 127) / 128));
-    if (H % dma::kBK == 0)
+    if (H % routedma::kSK == 0)
       hipLaunchKernelGGL(routedma::route_logits_dma_kernel, grid, dim3(dma::kThreads), 0, stream, x, planes, bias,
                          logits, T, H, E);
     else
