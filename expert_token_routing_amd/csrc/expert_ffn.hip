@@ -180,6 +180,15 @@ __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __re
                                          int r0) {
   const int w = threadIdx.x >> 6, wm = w % kWR, wn = w / kWR;
   const int lane = lane_id();
+  // GEMM1 multiplies weight x row fragments, i.e. produces the transposed
+  // tile, so that each lane ends up with 4 consecutive h columns of one row
+  // (8-byte stores); GEMM2 keeps the direct form (a column per lane).
+  auto mma = [](const u32x4& ra, const u32x4& wb, const f32x4v& c) {
+    if constexpr (SWIGLU)
+      return mfma16x16x32(wb, ra, c);
+    else
+      return mfma16x16x32(ra, wb, c);
+  };
   // stages of kSK; K is a multiple of 32, so the last stage may hold only
   // its first k step (the second is multiplied as zeros)
   const int nk = (K + kSK - 1) / kSK;
@@ -237,7 +246,7 @@ __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __re
 #pragma unroll
       for (int i = 0; i < FMT; ++i) {
 #pragma unroll
-        for (int j = 0; j < kFN; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < kFN; ++j) acc[i][j] = mma(a[i], b[j], acc[i][j]);
         a[i] = read_a<1>(cA, fa, i);
       }
 #pragma unroll
@@ -254,7 +263,7 @@ __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __re
 #pragma unroll
     for (int i = 0; i < kH1; ++i)
 #pragma unroll
-      for (int j = 0; j < kFN; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < kFN; ++j) acc[i][j] = mma(a[i], b[j], acc[i][j]);
     __builtin_amdgcn_sched_barrier(0);
     // every wave has read stage kt (its reads were waited for), and stage
     // kt+1 landed: refill stage kt's buffer with stage kt+kStages, read stage kt+1
@@ -274,7 +283,7 @@ __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __re
 #pragma unroll
     for (int i = kH1; i < FMT; ++i) {
 #pragma unroll
-      for (int j = 0; j < kFN; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < kFN; ++j) acc[i][j] = mma(a[i], b[j], acc[i][j]);
       a[i] = read_a<0>(nA, fa, i);
     }
 #pragma unroll
@@ -283,35 +292,41 @@ __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __re
   }
   dma::wait_lds_barrier();
 
-  // C: fragment (i, j) lane l -> tile row 16 (kWR i + wm) + 4 (l >> 4) + v,
-  // tile column 64 wn + 16 j + (l & 15).
-  if (SWIGLU) {
+  const int l16 = lane & 15;        // lane within a 16-lane group
+  const int g4 = 4 * (lane >> 4);   // 4 x the lane's group
+  if constexpr (SWIGLU) {
+    // transposed tile: fragment (i, j), lane l, element v is tile row
+    // 16 (kWR i + wm) + (l & 15), tile column 64 wn + 16 j + 4 (l >> 4) + v;
     // wave columns: 32 gate then the matching 32 up outputs
 #pragma unroll
     for (int i = 0; i < FMT; ++i) {
+      const int row = 16 * (kWR * i + wm) + l16;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int col = out_c0 + 32 * wn + 16 * j + (lane & 15);
+        const int col = out_c0 + 32 * wn + 16 * j + g4;
+        if (row < rows && col < N) {  // N is a multiple of 8: all 4 columns are in range
+          float hv[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = 16 * (kWR * i + wm) + 4 * (lane >> 4) + v;
-          if (row < rows && col < N) {
+          for (int v = 0; v < 4; ++v) {
             const float g = acc[i][j][v];
-            const float u = acc[i][j + 2][v];
-            C[int64_t(r0 + row) * ldc + col] = uint16_t(f32_to_bf16_bits(g / (1.f + __expf(-g)) * u));
+            hv[v] = g / (1.f + __expf(-g)) * acc[i][j + 2][v];
           }
+          *reinterpret_cast<uint2*>(C + int64_t(r0 + row) * ldc + col) =
+              make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
         }
       }
     }
   } else {
+    // fragment (i, j), lane l, element v is tile row 16 (kWR i + wm) + 4 (l >> 4) + v,
+    // tile column 64 wn + 16 j + (l & 15)
 #pragma unroll
     for (int i = 0; i < FMT; ++i)
 #pragma unroll
       for (int j = 0; j < kFN; ++j) {
-        const int col = out_c0 + 64 * wn + 16 * j + (lane & 15);
+        const int col = out_c0 + 64 * wn + 16 * j + l16;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int row = 16 * (kWR * i + wm) + 4 * (lane >> 4) + v;
+          const int row = 16 * (kWR * i + wm) + g4 + v;
           if (row < rows && col < N) C[int64_t(r0 + row) * ldc + col] = uint16_t(f32_to_bf16_bits(acc[i][j][v]));
         }
       }
