@@ -19,7 +19,8 @@
 //      the same expert, found with one ballot per distinct expert) and fills
 //      perm_src and inv;
 //   4. copy: one wave per token reads the token vector once and writes it to
-//      each of its rows.
+//      each of its rows, with non-temporal stores (the rows are not read
+//      again soon, so they should not evict other data from the caches).
 #include "gemm_tile.h"
 #include "moe_kernels.h"
 
@@ -70,15 +71,36 @@ dispatch_index_kernel(const int32_t* __restrict__ topk_idx, const int32_t* __res
   __shared__ int s_seg[1024 + 1];
   __shared__ int s_base[4][1024];
   __shared__ int s_tmp[4];
-  // Segment starts: exclusive scan of the local experts' counts (4 per thread).
+  const int wv = threadIdx.x >> 6;
+  const int c = blockIdx.x * 4 + wv;
+  const int lane = lane_id();
+  const int t = c * kChunk + lane;
+  const bool valid = c < nchunks && t < T;
+  // All independent global loads first, so that their latencies overlap:
+  // this lane's selections, the local experts' counts (4 per thread), and this
+  // chunk's offset inside every local segment (16 per lane at most).
+  int ev[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) ev[j] = (j < k && valid) ? topk_idx[int64_t(t) * k + j] : -1;
   int cnt[4];
-  int sum = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int i = threadIdx.x * 4 + q;
     cnt[q] = i < E_local ? counts[e0 + i] : 0;
-    sum += cnt[q];
   }
+  int cb[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int i = lane + 64 * q;
+    cb[q] = (c < nchunks && i < E_local) ? chunk_base[int64_t(e0 + i) * nchunks + c] : 0;
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int i = lane + 64 * q;
+    if (i < E_local) s_base[wv][i] = cb[q];
+  }
+  // Segment starts: exclusive scan of the local experts' counts.
+  int sum = cnt[0] + cnt[1] + cnt[2] + cnt[3];
   int tot;
   int pre = block_exclusive_scan(sum, s_tmp, tot);
 #pragma unroll
@@ -92,25 +114,12 @@ dispatch_index_kernel(const int32_t* __restrict__ topk_idx, const int32_t* __res
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= E_local; i += kThreads) offsets[i] = s_seg[i];
 
-  const int wv = threadIdx.x >> 6;
-  const int c = blockIdx.x * 4 + wv;
-  const int lane = lane_id();
-  // This chunk's offset inside every local expert's segment, staged in LDS so
-  // that the loop below reads no global memory.
-  if (c < nchunks)
-    for (int i = lane; i < E_local; i += 64) s_base[wv][i] = chunk_base[int64_t(e0 + i) * nchunks + c];
-  __syncthreads();
   if (c >= nchunks) return;
-  const int t = c * kChunk + lane;
-  const bool valid = t < T;
-  int ev[KMAX];
   uint32_t pend = 0;
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
-    ev[j] = -1;
     if (j < k && valid) {
-      const int e = topk_idx[int64_t(t) * k + j];
-      ev[j] = e;
+      const int e = ev[j];
       if (e >= e0 && e < e0 + E_local)
         pend |= 1u << j;
       else
@@ -171,7 +180,7 @@ dispatch_copy_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int v = v0 + u * 64 + lane;
-        if (v < nv) dst[v] = q[u];
+        if (v < nv) __builtin_nontemporal_store(q[u], dst + v);
       }
     }
   }
