@@ -171,6 +171,21 @@ namespace panelffn {
 
 using namespace dma::panel;
 
+// Ask the scheduler to alternate the region's MFMAs with its LDS reads, one
+// read after each MFMA while reads remain, so that the reads spread over the
+// MFMA time instead of bunching up (a read that must wait for an earlier MFMA
+// simply takes a later slot).
+template <int NM, int NR>
+__device__ __forceinline__ void alternate_mfma_reads() {
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // one MFMA
+    if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // one LDS read
+  }
+#pragma unroll
+  for (int i = NM; i < NR; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+}
+
 // One tile: FMT fragments per wave row (16 * kWR * FMT >= rows), `rows` rows
 // from the row source, weight columns given by col_of.
 template <int FMT, bool SWIGLU, typename SrcRow, typename ColOf>
@@ -249,6 +264,7 @@ __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __re
         for (int j = 0; j < kFN; ++j) acc[i][j] = mma(a[i], b[j], acc[i][j]);
         a[i] = read_a<1>(cA, fa, i);
       }
+      alternate_mfma_reads<FMT * kFN, 2 * kFN + FMT>();
 #pragma unroll
       for (int j = 0; j < kFN; ++j) b[j] = bs[j];
       if (half_tail && kt == nk - 1) {  // k beyond K: LDS holds other data
@@ -286,6 +302,7 @@ __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __re
       for (int j = 0; j < kFN; ++j) acc[i][j] = mma(a[i], b[j], acc[i][j]);
       a[i] = read_a<0>(nA, fa, i);
     }
+    alternate_mfma_reads<(FMT - kH1) * kFN, 2 * kFN + FMT>();
 #pragma unroll
     for (int j = 0; j < kFN; ++j) b[j] = bn[j];
     __builtin_amdgcn_sched_barrier(0);
