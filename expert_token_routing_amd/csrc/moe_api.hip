@@ -53,7 +53,7 @@ static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 // Workspace layout of moe_forward.
 struct ForwardLayout {
-  size_t planes, logits, topk_idx, topk_w, counts, offsets, perm_src, inv, chunks, x_perm, h, out, total;
+  size_t planes, part, logits, topk_idx, topk_w, counts, offsets, perm_src, inv, chunks, x_perm, h, out, total;
 };
 static ForwardLayout forward_layout(int T, int H, int I, int E, int k, int E_local) {
   ForwardLayout L{};
@@ -66,6 +66,7 @@ static ForwardLayout forward_layout(int T, int H, int I, int E, int k, int E_loc
     return at;
   };
   L.planes = take(size_t(3) * E * H * sizeof(uint16_t));
+  L.part = take(size_t(T) * E * sizeof(float));
   L.logits = take(size_t(T) * E * sizeof(float));
   L.topk_idx = take(size_t(T) * k * sizeof(int32_t));
   L.topk_w = take(size_t(T) * k * sizeof(float));
@@ -99,10 +100,9 @@ const char* moe_status_string(int status) {
 }
 
 size_t moe_route_workspace_size(int T, int H, int E, int k) {
-  (void)T;
   (void)k;
-  if (H <= 0 || E <= 0) return 0;
-  return align_up(size_t(3) * E * H * sizeof(uint16_t));
+  if (H <= 0 || E <= 0 || T < 0) return 0;
+  return align_up(size_t(3) * E * H * sizeof(uint16_t)) + align_up(size_t(T) * E * sizeof(float));
 }
 
 int moe_route(const moe_bf16* x, const float* w_router, const float* bias, int T, int H, int E, int k,
@@ -116,8 +116,11 @@ int moe_route(const moe_bf16* x, const float* w_router, const float* bias, int T
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0 ||
       workspace_bytes < moe_route_workspace_size(T, H, E, k))
     return MOE_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
   return hip_status(launch_route(x, w_router, bias, T, H, E, k, renormalize, logits, topk_idx, topk_w,
-                                 static_cast<uint16_t*>(workspace), stream));
+                                 reinterpret_cast<uint16_t*>(ws),
+                                 reinterpret_cast<float*>(ws + align_up(size_t(3) * E * H * sizeof(uint16_t))),
+                                 stream));
 }
 
 size_t moe_dispatch_workspace_size(int T, int E, int k) {
@@ -214,7 +217,7 @@ static int forward_impl(const moe_bf16* x, const float* w_router, const float* b
   hipError_t err = mark(0);
   if (err == hipSuccess)
     err = launch_route(x, w_router, bias, T, H, E, k, renormalize, logits, topk_idx, topk_w,
-                       static_cast<uint16_t*>(at(L.planes)), stream);
+                       static_cast<uint16_t*>(at(L.planes)), static_cast<float*>(at(L.part)), stream);
   if (err == hipSuccess) err = mark(1);
   // GEMM1 reads the token vectors in place when it can, so dispatch only
   // builds the tables; otherwise the rows are copied out first.

@@ -103,49 +103,61 @@ route_logits_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
     }
 }
 
-// Same logits through the direct-to-LDS pipeline (H a multiple of 64): tiles
-// of 128 tokens x 128 experts, 8 waves of 64 x 32. The token rows and the
-// three weight planes come in 64-deep stages (every request a whole 128-byte
-// line) through two LDS buffers; stage s + 2 is issued right after the
-// barrier at which every wave has finished reading stage s.
+// Same logits through the direct-to-LDS pipeline (H a multiple of 64), with
+// the k range split in two halves that run as separate workgroups
+// (blockIdx.z): tiles of 256 tokens x 128 experts per half, 8 waves of
+// 64 x 64 (each token fragment read from LDS serves 2 x 3 products, each
+// weight fragment 2), so LDS reads per product are about a quarter lower than
+// with 128 x 128 tiles while there are still 256 workgroups for T = 16384,
+// E = 256. The token rows and the three weight planes come in 64-deep stages
+// (every request a whole 128-byte line) through two LDS buffers; stage s + 2
+// is issued right after the barrier at which every wave has finished reading
+// stage s. Half z writes its raw partial sums to out[z]; the top-k kernel
+// adds the two halves and the bias in a fixed order.
 namespace routedma {
 
-constexpr int kBM = 128, kBN = 128, kFM = 2, kPlanes = 3;
+constexpr int kBM = 256, kBN = 128, kFM = 2, kFN = 2, kPlanes = 3;
 constexpr int kSK = 64;                                            // k per stage
-constexpr int kRowStage = 128 * kSK * 2;                           // 16 KiB per 128-row operand
-constexpr int kStage = kRowStage * (1 + kPlanes);                  // tokens + 3 planes
+constexpr int kAStage = kBM * kSK * 2;                             // 32 KiB of token rows
+constexpr int kPStage = kBN * kSK * 2;                             // 16 KiB per weight plane
+constexpr int kStage = kAStage + kPlanes * kPStage;                // 80 KiB
 constexpr int kBufs = 2;
 
 __global__ void __launch_bounds__(dma::kThreads)
-route_logits_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes,
-                        const float* __restrict__ bias, float* __restrict__ logits, int T, int H, int E) {
+route_logits_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes, float* __restrict__ out0,
+                        float* __restrict__ out1, int T, int H, int E) {
   using namespace dma;
   __shared__ __attribute__((aligned(1024))) char smem[kBufs * kStage];
   MOE_LDS char* lds = (MOE_LDS char*)smem;
   const int t0 = blockIdx.x * kBM;
   const int n0 = blockIdx.y * kBN;
-  const int w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
+  const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
   const int lane = lane_id();
-  const int nk = H / kSK;
+  const int nk_all = H / kSK;
+  const int half = (nk_all + 1) / 2;
+  const int s0 = blockIdx.z * half;
+  const int nk = max(0, min(nk_all, s0 + half) - s0);  // stages of this half
   const int64_t plane = int64_t(E) * H;
+  float* __restrict__ out = blockIdx.z == 0 ? out0 : out1;
 
-  RowLoader64<128> la, lb[kPlanes];
+  RowLoader64<kBM> la;
+  RowLoader64<kBN> lb[kPlanes];
   la.init(x + int64_t(t0) * H, H, min(kBM, T - t0));
 #pragma unroll
   for (int p = 0; p < kPlanes; ++p) lb[p].init(planes + p * plane + int64_t(n0) * H, H, min(kBN, E - n0));
   auto issue = [&](int st) {
     if (st < nk) {
       MOE_LDS char* dst = lds + (st % kBufs) * kStage;
-      la.issue(dst, st * kSK);
+      la.issue(dst, (s0 + st) * kSK);
 #pragma unroll
-      for (int p = 0; p < kPlanes; ++p) lb[p].issue(dst + (1 + p) * kRowStage, st * kSK);
+      for (int p = 0; p < kPlanes; ++p) lb[p].issue(dst + kAStage + p * kPStage, (s0 + st) * kSK);
     }
   };
   // fragment offsets of 16-deep step ks (0..3): A rows wm*64 + fm*32 + lane%32,
-  // B rows wn*32 + lane%32, chunk 2 ks + lane/32, swizzled as RowLoader64
+  // B rows wn*64 + fn*32 + lane%32, chunk 2 ks + lane/32, swizzled as RowLoader64
   const int khalf = lane >> 5;
   const int ma = wm * 64 + (lane & 31);
-  const int mb = wn * 32 + (lane & 31);
+  const int mb = wn * 64 + (lane & 31);
   uint32_t aoff[kSK / 16], boff[kSK / 16];
 #pragma unroll
   for (int ks = 0; ks < kSK / 16; ++ks) {
@@ -154,7 +166,7 @@ route_logits_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
   }
   struct F {
     u32x4 a[kFM];
-    u32x4 b[kPlanes];
+    u32x4 b[kPlanes][kFN];
   };
   auto load = [&](const MOE_LDS char* st, int ks, F& f) {
 #pragma unroll
@@ -162,72 +174,83 @@ route_logits_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
       f.a[fm] = *reinterpret_cast<const MOE_LDS u32x4*>(st + aoff[ks] + fm * 32 * 128);
 #pragma unroll
     for (int p = 0; p < kPlanes; ++p)
-      f.b[p] = *reinterpret_cast<const MOE_LDS u32x4*>(st + (1 + p) * kRowStage + boff[ks]);
+#pragma unroll
+      for (int fn = 0; fn < kFN; ++fn)
+        f.b[p][fn] = *reinterpret_cast<const MOE_LDS u32x4*>(st + kAStage + p * kPStage + boff[ks] + fn * 32 * 128);
   };
-  f32x16 acc[kFM];
+  f32x16 acc[kFM][kFN];
 #pragma unroll
   for (int fm = 0; fm < kFM; ++fm)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[fm][v] = 0.f;
+    for (int fn = 0; fn < kFN; ++fn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
   auto mma = [&](const F& f) {
 #pragma unroll
     for (int p = 0; p < kPlanes; ++p)
 #pragma unroll
-      for (int fm = 0; fm < kFM; ++fm) acc[fm] = mfma32x32x16(f.a[fm], f.b[p], acc[fm]);
+      for (int fm = 0; fm < kFM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < kFN; ++fn) acc[fm][fn] = mfma32x32x16(f.a[fm], f.b[p][fn], acc[fm][fn]);
   };
   auto interleave = [&]() {
+    constexpr int kM = kFM * kFN * kPlanes, kR = kFM + kPlanes * kFN;
 #pragma unroll
-    for (int i = 0; i < kFM * kPlanes; ++i) {
+    for (int i = 0; i < kM; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < kFM + kPlanes) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < kR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
-  constexpr int kLoads = (1 + kPlanes) * RowLoader64<128>::kPer;  // DMA instructions per wave per stage
+  constexpr int kLoads = RowLoader64<kBM>::kPer + kPlanes * RowLoader64<kBN>::kPer;  // DMA instructions per wave per stage
 
-  issue(0);
-  issue(1);
-  if (nk > 1)
-    wait_vm_barrier<kLoads>();
-  else
-    wait_vm_barrier<0>();
-  F f0, f1;
-  load(lds, 0, f0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const MOE_LDS char* cur = lds + (kt % kBufs) * kStage;
-    // steps 0..2: each step's MFMAs cover the next step's LDS reads
-    load(cur, 1, f1);
-    mma(f0);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    load(cur, 2, f0);
-    mma(f1);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    load(cur, 3, f1);
-    mma(f0);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    // step 3: every wave is done reading stage kt and stage kt+1 (the only
-    // one in flight) landed; refill this buffer with stage kt+2
-    wait_lgkm0();
-    wait_vm_barrier<0>();
-    issue(kt + 2);
-    load(lds + ((kt + 1) % kBufs) * kStage, 0, f0);  // stage nk: a finished buffer, values unused
-    mma(f1);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  wait_lgkm0();
-
-  const int e = n0 + mb;
-  const float b = (bias != nullptr && e < E) ? bias[e] : 0.f;
-#pragma unroll
-  for (int fm = 0; fm < kFM; ++fm)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int t = t0 + wm * 64 + fm * 32 + mfma_c_row(v, lane);
-      if (t < T && e < E) logits[int64_t(t) * E + e] = acc[fm][v] + b;
+  if (nk > 0) {
+    issue(0);
+    issue(1);
+    if (nk > 1)
+      wait_vm_barrier<kLoads>();
+    else
+      wait_vm_barrier<0>();
+    F f0, f1;
+    load(lds, 0, f0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const MOE_LDS char* cur = lds + (kt % kBufs) * kStage;
+      // steps 0..2: each step's MFMAs cover the next step's LDS reads
+      load(cur, 1, f1);
+      mma(f0);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      load(cur, 2, f0);
+      mma(f1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      load(cur, 3, f1);
+      mma(f0);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      // step 3: every wave is done reading stage kt and stage kt+1 (the only
+      // one in flight) landed; refill this buffer with stage kt+2
+      wait_lgkm0();
+      wait_vm_barrier<0>();
+      issue(kt + 2);
+      load(lds + ((kt + 1) % kBufs) * kStage, 0, f0);  // stage nk: a finished buffer, values unused
+      mma(f1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
     }
+    wait_lgkm0();
+  }
+
+#pragma unroll
+  for (int fn = 0; fn < kFN; ++fn) {
+    const int e = n0 + mb + fn * 32;
+#pragma unroll
+    for (int fm = 0; fm < kFM; ++fm)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int t = t0 + wm * 64 + fm * 32 + mfma_c_row(v, lane);
+        if (t < T && e < E) out[int64_t(t) * E + e] = acc[fm][fn][v];
+      }
+  }
 }
 
 }  // namespace routedma
@@ -238,19 +261,32 @@ route_logits_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
 // LDS) and then the lowest expert id holding it (one ballot per EPL slot).
 template <int EPL>
 __global__ void __launch_bounds__(kThreads)
-route_topk_kernel(const float* __restrict__ logits, int T, int E, int k, int renormalize,
-                  int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+route_topk_kernel(float* __restrict__ logits, const float* __restrict__ part, const float* __restrict__ bias, int T,
+                  int E, int k, int renormalize, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
   const int lane = lane_id();
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* row = logits + int64_t(t) * E;
+  float* row = logits + int64_t(t) * E;
   float v[EPL];
   uint32_t live = 0;  // bit i: expert lane + 64 i exists and is not taken yet
   float lm = -INFINITY;
+  if (part != nullptr) {  // logits hold the first k half: add the second, then the bias; store the sum
+    const float* prow = part + int64_t(t) * E;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E) {
+        const float l = (row[e] + prow[e]) + (bias != nullptr ? bias[e] : 0.f);
+        row[e] = l;
+        v[i] = l;
+      }
+    }
+  }
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + 64 * i;
-    v[i] = e < E ? row[e] : -INFINITY;
+    if (part == nullptr) v[i] = e < E ? row[e] : -INFINITY;
+    if (e >= E) v[i] = -INFINITY;
     if (e < E) {
       live |= 1u << i;
       lm = fmaxf(lm, v[i]);
@@ -303,7 +339,7 @@ route_topk_kernel(const float* __restrict__ logits, int T, int E, int k, int ren
 // Host-side launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_route(const uint16_t* x, const float* w_router, const float* bias, int T, int H, int E, int k,
-                        int renormalize, float* logits, int32_t* topk_idx, float* topk_w, uint16_t* planes,
+                        int renormalize, float* logits, int32_t* topk_idx, float* topk_w, uint16_t* planes, float* part,
                         hipStream_t stream) {
   const int64_t n = int64_t(E) * H;
   {
@@ -313,29 +349,38 @@ hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
+  const bool split = H % routedma::kSK == 0;
   {
-    dim3 grid(unsigned((T + 127) / 128), unsigned((E + 127) / 128));
-    if (H % routedma::kSK == 0)
-      hipLaunchKernelGGL(routedma::route_logits_dma_kernel, grid, dim3(dma::kThreads), 0, stream, x, planes, bias,
-                         logits, T, H, E);
-    else
+    if (split) {
+      dim3 grid(unsigned((T + routedma::kBM - 1) / routedma::kBM), unsigned((E + routedma::kBN - 1) / routedma::kBN),
+                2u);
+      hipLaunchKernelGGL(routedma::route_logits_dma_kernel, grid, dim3(dma::kThreads), 0, stream, x, planes, logits,
+                         part, T, H, E);
+    } else {
+      dim3 grid(unsigned((T + 127) / 128), unsigned((E + 127) / 128));
       hipLaunchKernelGGL(route_logits_kernel, grid, dim3(kThreads), 0, stream, x, planes, bias, logits, T, H, E);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   {
+    const float* pt = split ? part : nullptr;
     dim3 grid(unsigned((T + 3) / 4));
     const int epl = (E + 63) / 64;
+#define MOE_TOPK_LAUNCH(EPL)                                                                                       \
+  hipLaunchKernelGGL(route_topk_kernel<EPL>, grid, dim3(kThreads), 0, stream, logits, pt, bias, T, E, k, renormalize, \
+                     topk_idx, topk_w)
     if (epl <= 1)
-      hipLaunchKernelGGL(route_topk_kernel<1>, grid, dim3(kThreads), 0, stream, logits, T, E, k, renormalize, topk_idx, topk_w);
+      MOE_TOPK_LAUNCH(1);
     else if (epl <= 2)
-      hipLaunchKernelGGL(route_topk_kernel<2>, grid, dim3(kThreads), 0, stream, logits, T, E, k, renormalize, topk_idx, topk_w);
+      MOE_TOPK_LAUNCH(2);
     else if (epl <= 4)
-      hipLaunchKernelGGL(route_topk_kernel<4>, grid, dim3(kThreads), 0, stream, logits, T, E, k, renormalize, topk_idx, topk_w);
+      MOE_TOPK_LAUNCH(4);
     else if (epl <= 8)
-      hipLaunchKernelGGL(route_topk_kernel<8>, grid, dim3(kThreads), 0, stream, logits, T, E, k, renormalize, topk_idx, topk_w);
+      MOE_TOPK_LAUNCH(8);
     else
-      hipLaunchKernelGGL(route_topk_kernel<16>, grid, dim3(kThreads), 0, stream, logits, T, E, k, renormalize, topk_idx, topk_w);
+      MOE_TOPK_LAUNCH(16);
+#undef MOE_TOPK_LAUNCH
     return hipGetLastError();
   }
 }

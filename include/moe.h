@@ -69,7 +69,8 @@ const char* moe_status_string(int status);
 /* ------------------------------------------------------------------------ */
 
 /* Bytes of device workspace moe_route needs (a bfloat16 three-way split of
- * the float32 router weight). */
+ * the float32 router weight, and float32 partial logits of one half of the
+ * hidden dimension). */
 size_t moe_route_workspace_size(int T, int H, int E, int k);
 
 /*
