@@ -9,7 +9,8 @@
 // Parallelism (EP)", "Why a Single All-Reduce/Reduce-Scatter Works").
 //
 // One wave per token; the sum runs in float32 over the slots in order and is
-// rounded to bf16 once.
+// rounded to bf16 once. The expert rows are read with non-temporal loads: each
+// is read exactly once, so it should not evict other data from the caches.
 #include "gemm_tile.h"
 #include "moe_kernels.h"
 
@@ -59,7 +60,7 @@ combine_kernel(const uint16_t* __restrict__ expert_out, const int32_t* __restric
 #pragma unroll
       for (int u = 0; u < U; ++u)
         if (j < nl && v0 + 64 * u < nv)
-          q[j][u] = reinterpret_cast<const u32x4*>(expert_out + int64_t(rows[j]) * H)[v0 + 64 * u];
+          q[j][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(expert_out + int64_t(rows[j]) * H) + v0 + 64 * u);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (v0 + 64 * u >= nv) break;
