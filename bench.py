@@ -57,6 +57,10 @@ def parse():
                     help="print the markdown summary of two rocprofv3 --pmc output folders and exit")
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="extra steps timed with a 1 GiB write between them (evicts L2 / Infinity Cache); 0 = off")
+    ap.add_argument("--ep-sweep", default="",
+                    help="comma-separated EP degrees (e.g. 1,2,4,8,16,32,64): instead of the single share, time "
+                         "every rank's share of the workload's whole layer (e0 = r * E/ep) at each degree and "
+                         "print one JSON line with the layer time per degree (max over ranks)")
     return ap.parse_args()
 
 
@@ -183,6 +187,98 @@ def cpu_baseline(inp, sample_tokens):
                       f"float64 numpy ({blas_name}), one run of {dt:.1f} s on {cpu}"}
 
 
+def ep_sweep(args):
+    """Every rank's share of the workload's whole layer at each EP degree,
+    run one after another on this GPU. Under expert parallelism the ranks run
+    their shares side by side, so the layer time at degree ep (before the
+    exchange of partial outputs) is the slowest rank's share time."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    import expert_token_routing_amd as M
+    import workloads as W
+
+    base = W.CONFIGS[args.workload]
+    degrees = [int(v) for v in args.ep_sweep.split(",") if v.strip()]
+    for ep in degrees:
+        if ep < 1 or base.E % ep:
+            sys.exit(f"--ep-sweep: EP degree {ep} does not divide E = {base.E}")
+    cfg = dataclasses.replace(base, name=base.name + "_layer", e0=0, E_local=base.E)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[sweep] generating {cfg.name} inputs (all {cfg.E} experts)")
+    inp = W.make_inputs(cfg)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x = bf(inp.x)
+    wr = torch.from_numpy(inp.w_router).to(dev)
+    bias = None if inp.bias is None else torch.from_numpy(inp.bias).to(dev)
+    gu = bf(inp.w_gate_up)
+    dn = bf(inp.w_down)
+    del inp
+    y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps + 1)]
+    for row in evs:
+        for ev in row:
+            ev.record(stream)  # creates the underlying HIP event
+    rows = []
+    for ep in degrees:
+        El = cfg.E // ep
+        ws = torch.empty(M.forward_workspace_size(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, El), dtype=torch.uint8,
+                         device=dev)
+        lay = M.forward_workspace_layout(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, El)
+        share_ms, stage_ms, n_rows = [], [], []
+        log(f"[sweep] ep={ep} E_local={El}: {ep} shares")
+        for r in range(ep):
+            gu_r, dn_r = gu[r * El:(r + 1) * El], dn[r * El:(r + 1) * El]
+            for _ in range(args.warmup):
+                M.moe_forward_profiled(x, wr, bias, gu_r, dn_r, cfg.k, r * El, cfg.renormalize, y, ws, evs[0],
+                                       stream=stream)
+            for i in range(args.steps):
+                M.moe_forward_profiled(x, wr, bias, gu_r, dn_r, cfg.k, r * El, cfg.renormalize, y, ws,
+                                       evs[i + 1], stream=stream)
+            torch.cuda.synchronize()
+            st = np.array([[evs[i + 1][j].elapsed_time(evs[i + 1][j + 1]) for j in range(5)]
+                           for i in range(args.steps)]).mean(0)
+            stage_ms.append(st)
+            share_ms.append(float(st.sum()))
+            n_rows.append(int(ws[lay["offsets"] + 4 * El:lay["offsets"] + 4 * El + 4].view(torch.int32).item()))
+        share_ms = np.array(share_ms)
+        stage_ms = np.array(stage_ms)
+        n_rows = np.array(n_rows)
+        gemm_ms = stage_ms[:, 2] + stage_ms[:, 3]
+        gemm_tf = 6.0 * n_rows * cfg.H * cfg.I / (gemm_ms * 1e-3) / 1e12
+        worst = int(share_ms.argmax())
+        rows.append({
+            "ep": ep, "E_local": El,
+            "layer_ms": round(float(share_ms.max()), 4),
+            "layer_tokens_per_s": round(cfg.T / (share_ms.max() * 1e-3), 1),
+            "share_ms_mean": round(float(share_ms.mean()), 4),
+            "imbalance_max_over_mean": round(float(share_ms.max() / share_ms.mean()), 4),
+            "rows_per_rank_max": int(n_rows.max()), "rows_per_rank_mean": round(float(n_rows.mean()), 1),
+            "grouped_gemm_tflops_mean": round(float(gemm_tf.mean()), 2),
+            "grouped_gemm_frac_mfma_bf16_mean": round(float(gemm_tf.mean()) / PEAK_BF16_TFLOPS, 4),
+            "slowest_rank": worst,
+            "slowest_rank_stage_us": {n: round(float(v) * 1e3, 2) for n, v in zip(STAGES, stage_ms[worst])},
+        })
+        log(f"[sweep] ep={ep}: layer {share_ms.max():.3f} ms (mean share {share_ms.mean():.3f} ms), "
+            f"GEMM {gemm_tf.mean():.0f} TFLOP/s")
+        del ws
+    print(json.dumps({
+        "metric": "EP-share sweep: layer time at each EP degree = slowest rank's share (partial-output exchange "
+                  "not included), every share run on this one GPU",
+        "workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "k": cfg.k,
+        "renormalize": cfg.renormalize, "steps_per_share": args.steps, "warmup_per_share": args.warmup,
+        "dtype": "bf16", "data": "synthetic (seeded numpy PCG64, shapes of the named workload; no trained weights)",
+        "rows": rows,
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_counters:
@@ -193,6 +289,9 @@ def main():
         print("bench.py measures one GPU's share of the MoE layer; runs on more than one GPU are not part "
               "of this build (--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
+    if args.ep_sweep:
+        ep_sweep(args)
+        return
 
     import numpy as np
     import torch
@@ -302,6 +401,32 @@ def main():
     d_ms = float(np.mean([dev_ev[i].elapsed_time(dev_ev[i + 1]) for i in range(nd)]))
     del d_out, d_ws
 
+    # the combine alone, bf16 output and float32 partial output, on the
+    # forward's own expert outputs, selections and weights
+    n_out = max(N, 1)
+    c_out = ws[lay["expert_out"]:lay["expert_out"] + 2 * n_out * cfg.H].view(torch.bfloat16).view(n_out, cfg.H)
+    c_inv = ws[lay["inv"]:lay["inv"] + 4 * cfg.T * cfg.k].view(torch.int32)
+    c_w = ws[lay["topk_w"]:lay["topk_w"] + 4 * cfg.T * cfg.k].view(torch.float32).view(cfg.T, cfg.k)
+    y32 = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=dev)
+    y16 = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    comb_ms = {}
+    for name, fn, yy in (("bf16", M.moe_combine, y16), ("f32", M.moe_combine_f32, y32)) * 2:
+        fn(c_out, c_inv, c_w, y=yy)
+        c_ev = [torch.cuda.Event(enable_timing=True) for _ in range(nd + 1)]
+        c_ev[0].record(stream)
+        for i in range(nd):
+            fn(c_out, c_inv, c_w, y=yy)
+            c_ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        comb_ms[name] = float(np.mean([c_ev[i].elapsed_time(c_ev[i + 1]) for i in range(nd)]))
+    f32_bytes = work["combine"]["bytes"] + 2.0 * cfg.T * cfg.H
+    f32_gbs = f32_bytes / (comb_ms["f32"] * 1e-3) / 1e9
+    combine_f32 = {"us": round(comb_ms["f32"] * 1e3, 2), "gbs": round(f32_gbs, 1),
+                   "frac_hbm": round(f32_gbs / PEAK_HBM_GBS, 4), "bf16_us": round(comb_ms["bf16"] * 1e3, 2),
+                   "note": "moe_combine_f32 (float32 partial output) and moe_combine, each timed alone on the "
+                           "forward's expert outputs"}
+    del y32, y16
+
     stages = {}
     for n, ms in zip(STAGES, stage_avg):
         s = {"us": round(float(ms) * 1e3, 2)}
@@ -349,6 +474,7 @@ def main():
         "grouped_gemm": {"tflops": round(gemm_tflops, 2), "frac_mfma_bf16": round(gemm_tflops / PEAK_BF16_TFLOPS, 4)},
         "stages": stages,
         "dispatch_rows": dispatch_rows,
+        "combine_f32": combine_f32,
         "layer_tflops": round(total_flop / (ms_per_step * 1e-3) / 1e12, 2),
         "realised": {"N_local_rows": N, "U_tokens_with_local_pick": U,
                      "rows_per_local_expert_max": int(np.diff(offs).max()),

@@ -29,10 +29,13 @@ SIGNATURES = {
                              _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "moe_expert_ffn": (c_int, [_P, _P, _P, _P, c_int, c_int, c_int, c_int64, _P, _P, _P]),
     "moe_combine": (c_int, [_P, _P, _P, c_int, c_int, c_int, _P, _P]),
+    "moe_combine_f32": (c_int, [_P, _P, _P, c_int, c_int, c_int, _P, _P]),
     "moe_forward_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int]),
     "moe_forward_workspace_layout": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(c_size_t)]),
     "moe_forward": (c_int, [_P, _P, _P, _P, _P, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                             _P, _P, c_size_t, _P]),
+    "moe_forward_f32": (c_int, [_P, _P, _P, _P, _P, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                _P, _P, c_size_t, _P]),
     "moe_forward_profiled": (c_int, [_P, _P, _P, _P, _P, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                      _P, _P, c_size_t, _P, _P]),
 }
@@ -178,8 +181,7 @@ def moe_expert_ffn(x_perm, offsets, w_gate_up, w_down, *, h=None, out=None, stre
     return h, out
 
 
-def moe_combine(expert_out, inv, topk_w, *, y=None, stream=None):
-    """y [T, H]: weighted sum of each token's local expert outputs."""
+def _combine(name, out_dtype, expert_out, inv, topk_w, y, stream):
     torch = _torch()
     _need(expert_out, torch.bfloat16, "expert_out", 2)
     _need(inv, torch.int32, "inv")
@@ -187,10 +189,23 @@ def moe_combine(expert_out, inv, topk_w, *, y=None, stream=None):
     T, k = topk_w.shape
     H = expert_out.shape[1]
     dev = expert_out.device
-    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if y is None else y
-    st = lib().moe_combine(_ptr(expert_out), _ptr(inv), _ptr(topk_w), T, H, k, _ptr(y), _stream(stream, dev))
-    check(st, "moe_combine")
+    y = torch.empty((T, H), dtype=out_dtype, device=dev) if y is None else y
+    _need(y, out_dtype, "y", 2)
+    if tuple(y.shape) != (T, H):
+        raise ValueError(f"y must have shape {(T, H)}, got {tuple(y.shape)}")
+    st = getattr(lib(), name)(_ptr(expert_out), _ptr(inv), _ptr(topk_w), T, H, k, _ptr(y), _stream(stream, dev))
+    check(st, name)
     return y
+
+
+def moe_combine(expert_out, inv, topk_w, *, y=None, stream=None):
+    """y [T, H] bf16: weighted sum of each token's local expert outputs."""
+    return _combine("moe_combine", _torch().bfloat16, expert_out, inv, topk_w, y, stream)
+
+
+def moe_combine_f32(expert_out, inv, topk_w, *, y=None, stream=None):
+    """y [T, H] float32: moe_combine's sums before their rounding to bf16."""
+    return _combine("moe_combine_f32", _torch().float32, expert_out, inv, topk_w, y, stream)
 
 
 def forward_workspace_size(T, H, I, E, k, E_local) -> int:
@@ -204,10 +219,7 @@ def forward_workspace_layout(T, H, I, E, k, E_local) -> dict:
     return dict(zip(names, [int(v) for v in arr]))
 
 
-def moe_forward(x, w_router, bias, w_gate_up, w_down, k, e0, renormalize=True, *, y=None, workspace=None,
-                stream=None):
-    """The rank's share of the MoE layer: y [T, H] bf16. ``E_local`` is
-    ``w_gate_up.shape[0]``; the rank owns experts [e0, e0 + E_local)."""
+def _forward(name, out_dtype, x, w_router, bias, w_gate_up, w_down, k, e0, renormalize, y, workspace, stream):
     torch = _torch()
     _need(x, torch.bfloat16, "x", 2)
     _need(w_router, torch.float32, "w_router", 2)
@@ -220,12 +232,32 @@ def moe_forward(x, w_router, bias, w_gate_up, w_down, k, e0, renormalize=True, *
     E_local, _, I2 = w_gate_up.shape
     I = I2 // 2
     dev = x.device
-    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev) if y is None else y
+    y = torch.empty((T, H), dtype=out_dtype, device=dev) if y is None else y
+    _need(y, out_dtype, "y", 2)
+    if tuple(y.shape) != (T, H):
+        raise ValueError(f"y must have shape {(T, H)}, got {tuple(y.shape)}")
     ws = _workspace(forward_workspace_size(T, H, I, E, k, E_local), dev, workspace)
-    st = lib().moe_forward(_ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate_up), _ptr(w_down), T, H, I, E, k, e0,
-                           E_local, int(bool(renormalize)), _ptr(y), _ptr(ws), ws.numel(), _stream(stream, dev))
-    check(st, "moe_forward")
+    st = getattr(lib(), name)(_ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate_up), _ptr(w_down), T, H, I, E, k,
+                              e0, E_local, int(bool(renormalize)), _ptr(y), _ptr(ws), ws.numel(),
+                              _stream(stream, dev))
+    check(st, name)
     return y, ws
+
+
+def moe_forward(x, w_router, bias, w_gate_up, w_down, k, e0, renormalize=True, *, y=None, workspace=None,
+                stream=None):
+    """The rank's share of the MoE layer: y [T, H] bf16. ``E_local`` is
+    ``w_gate_up.shape[0]``; the rank owns experts [e0, e0 + E_local)."""
+    return _forward("moe_forward", _torch().bfloat16, x, w_router, bias, w_gate_up, w_down, k, e0, renormalize, y,
+                    workspace, stream)
+
+
+def moe_forward_f32(x, w_router, bias, w_gate_up, w_down, k, e0, renormalize=True, *, y=None, workspace=None,
+                    stream=None):
+    """moe_forward with the share kept in float32 (y [T, H] float32), for
+    summing the shares of several ranks before one rounding."""
+    return _forward("moe_forward_f32", _torch().float32, x, w_router, bias, w_gate_up, w_down, k, e0, renormalize,
+                    y, workspace, stream)
 
 
 def moe_forward_profiled(x, w_router, bias, w_gate_up, w_down, k, e0, renormalize, y, workspace, events,

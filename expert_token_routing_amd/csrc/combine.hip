@@ -9,17 +9,20 @@
 // Parallelism (EP)", "Why a Single All-Reduce/Reduce-Scatter Works").
 //
 // One wave per token; the sum runs in float32 over the slots in order and is
-// rounded to bf16 once. The expert rows are read with non-temporal loads: each
-// is read exactly once, so it should not evict other data from the caches.
+// rounded to bf16 once, or stored as float32 as it stands (the partial-output
+// form: the shares of all ranks are summed afterwards, and a float32 share is
+// not rounded before that sum). The expert rows are read with non-temporal
+// loads: each is read exactly once, so it should not evict other data from the
+// caches.
 #include "gemm_tile.h"
 #include "moe_kernels.h"
 
 namespace moe {
 
-template <int KMAX>
+template <int KMAX, bool F32>
 __global__ void __launch_bounds__(kThreads)
 combine_kernel(const uint16_t* __restrict__ expert_out, const int32_t* __restrict__ inv,
-               const float* __restrict__ topk_w, int T, int H, int k, uint16_t* __restrict__ y) {
+               const float* __restrict__ topk_w, int T, int H, int k, void* __restrict__ y) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int lane = lane_id();
@@ -49,7 +52,8 @@ combine_kernel(const uint16_t* __restrict__ expert_out, const int32_t* __restric
   // a token with no local slot is written as +0.
   const float init = nl > 0 ? -0.f : 0.f;
   const int nv = H / 8;
-  u32x4* dst = reinterpret_cast<u32x4*>(y + int64_t(t) * H);
+  u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + int64_t(t) * H);
+  float4* dstf = reinterpret_cast<float4*>(static_cast<float*>(y) + int64_t(t) * H);
   // U vectors per lane per pass; all of a pass's loads are issued before the
   // first one is used, so each lane keeps up to U * nl loads in flight.
   constexpr int U = 2;
@@ -77,19 +81,26 @@ combine_kernel(const uint16_t* __restrict__ expert_out, const int32_t* __restric
           }
         }
       }
-      u32x4 o;
+      if constexpr (F32) {
+        const int v = v0 + 64 * u;
+        dstf[2 * v] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        dstf[2 * v + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+      } else {
+        u32x4 o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-      dst[v0 + 64 * u] = o;
+        for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+        dst[v0 + 64 * u] = o;
+      }
     }
   }
 }
 
-hipError_t launch_combine(const uint16_t* expert_out, const int32_t* inv, const float* topk_w, int T, int H, int k,
-                          uint16_t* y, hipStream_t stream) {
+template <bool F32>
+static void launch_combine_t(const uint16_t* expert_out, const int32_t* inv, const float* topk_w, int T, int H,
+                             int k, void* y, hipStream_t stream) {
   const dim3 grid(unsigned(ceil_div(T, 4)));
 #define MOE_COMBINE_LAUNCH(KM) \
-  hipLaunchKernelGGL(combine_kernel<KM>, grid, dim3(kThreads), 0, stream, expert_out, inv, topk_w, T, H, k, y)
+  hipLaunchKernelGGL((combine_kernel<KM, F32>), grid, dim3(kThreads), 0, stream, expert_out, inv, topk_w, T, H, k, y)
   if (k <= 1)
     MOE_COMBINE_LAUNCH(1);
   else if (k <= 2)
@@ -103,6 +114,14 @@ hipError_t launch_combine(const uint16_t* expert_out, const int32_t* inv, const 
   else
     MOE_COMBINE_LAUNCH(32);
 #undef MOE_COMBINE_LAUNCH
+}
+
+hipError_t launch_combine(const uint16_t* expert_out, const int32_t* inv, const float* topk_w, int T, int H, int k,
+                          void* y, bool y_f32, hipStream_t stream) {
+  if (y_f32)
+    launch_combine_t<true>(expert_out, inv, topk_w, T, H, k, y, stream);
+  else
+    launch_combine_t<false>(expert_out, inv, topk_w, T, H, k, y, stream);
   return hipGetLastError();
 }
 

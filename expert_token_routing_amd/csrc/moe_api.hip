@@ -159,14 +159,24 @@ int moe_expert_ffn(const moe_bf16* x_perm, const int32_t* offsets, const moe_bf1
   return hip_status(launch_expert_ffn(x_perm, offsets, w_gate_up, w_down, H, I, E_local, capacity, h, out, stream));
 }
 
-int moe_combine(const moe_bf16* expert_out, const int32_t* inv, const float* topk_w, int T, int H, int k,
-                moe_bf16* y, hipStream_t stream) {
+static int combine_impl(const moe_bf16* expert_out, const int32_t* inv, const float* topk_w, int T, int H, int k,
+                        void* y, bool y_f32, hipStream_t stream) {
   if (T < 0 || H <= 0 || (H % 8) != 0 || k < 1) return MOE_ERR_INVALID_ARG;
   if (k > kMaxK) return MOE_ERR_UNSUPPORTED;
   if (int64_t(T) * k >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!expert_out || !inv || !topk_w || !y || !aligned16(expert_out) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
-  return hip_status(launch_combine(expert_out, inv, topk_w, T, H, k, y, stream));
+  return hip_status(launch_combine(expert_out, inv, topk_w, T, H, k, y, y_f32, stream));
+}
+
+int moe_combine(const moe_bf16* expert_out, const int32_t* inv, const float* topk_w, int T, int H, int k,
+                moe_bf16* y, hipStream_t stream) {
+  return combine_impl(expert_out, inv, topk_w, T, H, k, y, false, stream);
+}
+
+int moe_combine_f32(const moe_bf16* expert_out, const int32_t* inv, const float* topk_w, int T, int H, int k,
+                    float* y, hipStream_t stream) {
+  return combine_impl(expert_out, inv, topk_w, T, H, k, y, true, stream);
 }
 
 size_t moe_forward_workspace_size(int T, int H, int I, int E, int k, int E_local) {
@@ -184,7 +194,7 @@ int moe_forward_workspace_layout(int T, int H, int I, int E, int k, int E_local,
 
 static int forward_impl(const moe_bf16* x, const float* w_router, const float* bias, const moe_bf16* w_gate_up,
                         const moe_bf16* w_down, int T, int H, int I, int E, int k, int e0, int E_local,
-                        int renormalize, moe_bf16* y, void* workspace, size_t workspace_bytes,
+                        int renormalize, void* y, bool y_f32, void* workspace, size_t workspace_bytes,
                         hipEvent_t* events, hipStream_t stream) {
   int st = check_route_dims(T, H, E, k);
   if (st != MOE_OK) return st;
@@ -233,7 +243,7 @@ static int forward_impl(const moe_bf16* x, const float* w_router, const float* b
   if (err == hipSuccess) err = mark(3);
   if (err == hipSuccess) err = launch_expert_gemm2(h, offsets, w_down, H, I, E_local, cap, out, stream);
   if (err == hipSuccess) err = mark(4);
-  if (err == hipSuccess) err = launch_combine(out, inv, topk_w, T, H, k, y, stream);
+  if (err == hipSuccess) err = launch_combine(out, inv, topk_w, T, H, k, y, y_f32, stream);
   if (err == hipSuccess) err = mark(5);
   return hip_status(err);
 }
@@ -241,8 +251,15 @@ static int forward_impl(const moe_bf16* x, const float* w_router, const float* b
 int moe_forward(const moe_bf16* x, const float* w_router, const float* bias, const moe_bf16* w_gate_up,
                 const moe_bf16* w_down, int T, int H, int I, int E, int k, int e0, int E_local, int renormalize,
                 moe_bf16* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return forward_impl(x, w_router, bias, w_gate_up, w_down, T, H, I, E, k, e0, E_local, renormalize, y, workspace,
-                      workspace_bytes, nullptr, stream);
+  return forward_impl(x, w_router, bias, w_gate_up, w_down, T, H, I, E, k, e0, E_local, renormalize, y, false,
+                      workspace, workspace_bytes, nullptr, stream);
+}
+
+int moe_forward_f32(const moe_bf16* x, const float* w_router, const float* bias, const moe_bf16* w_gate_up,
+                    const moe_bf16* w_down, int T, int H, int I, int E, int k, int e0, int E_local, int renormalize,
+                    float* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return forward_impl(x, w_router, bias, w_gate_up, w_down, T, H, I, E, k, e0, E_local, renormalize, y, true,
+                      workspace, workspace_bytes, nullptr, stream);
 }
 
 int moe_forward_profiled(const moe_bf16* x, const float* w_router, const float* bias, const moe_bf16* w_gate_up,
@@ -252,8 +269,8 @@ int moe_forward_profiled(const moe_bf16* x, const float* w_router, const float* 
   if (!events) return MOE_ERR_INVALID_ARG;
   for (int i = 0; i < 6; ++i)
     if (!events[i]) return MOE_ERR_INVALID_ARG;
-  return forward_impl(x, w_router, bias, w_gate_up, w_down, T, H, I, E, k, e0, E_local, renormalize, y, workspace,
-                      workspace_bytes, events, stream);
+  return forward_impl(x, w_router, bias, w_gate_up, w_down, T, H, I, E, k, e0, E_local, renormalize, y, false,
+                      workspace, workspace_bytes, events, stream);
 }
 
 }  // extern "C"

@@ -48,9 +48,9 @@ hipError_t launch_dispatch_index(const int32_t* topk_idx, int T, int E, int k, i
                                  int32_t* offsets, int32_t* perm_src, int32_t* inv, int32_t* chunk_table,
                                  hipStream_t stream);
 
-// Weighted top-k sum in token order.
+// Weighted top-k sum in token order; y is bf16, or float32 when y_f32.
 hipError_t launch_combine(const uint16_t* expert_out, const int32_t* inv, const float* topk_w, int T, int H, int k,
-                          uint16_t* y, hipStream_t stream);
+                          void* y, bool y_f32, hipStream_t stream);
 
 // Cached device facts of the current device.
 int device_cu_count();

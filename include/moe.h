@@ -177,6 +177,21 @@ int moe_expert_ffn(const moe_bf16* x_perm, const int32_t* offsets, const moe_bf1
 int moe_combine(const moe_bf16* expert_out, const int32_t* inv, const float* topk_w, int T, int H,
                 int k, moe_bf16* y, hipStream_t stream);
 
+/*
+ * moe_combine with a float32 output: the same float32 sum, stored without the
+ * final rounding. This is the partial-output form of an expert-parallel
+ * share: every rank's output is one partial sum of the layer, and the layer is
+ * their sum over ranks ("Expert Parallelism (EP)", "Why a Single
+ * All-Reduce/Reduce-Scatter Works"). Keeping the shares in float32 rounds the
+ * layer once, after that sum, instead of once per share. Rounding y to bf16
+ * (round to nearest even) gives moe_combine's y bit for bit.
+ *
+ *   y [T, H] f32 OUT (every row written), 16-byte aligned.
+ * Checks and status codes are moe_combine's.
+ */
+int moe_combine_f32(const moe_bf16* expert_out, const int32_t* inv, const float* topk_w, int T, int H,
+                    int k, float* y, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Whole share: route -> dispatch -> expert MLPs -> combine, one stream.     */
 /* ------------------------------------------------------------------------ */
@@ -196,6 +211,19 @@ int moe_forward(const moe_bf16* x, const float* w_router, const float* bias,
                 const moe_bf16* w_gate_up, const moe_bf16* w_down, int T, int H, int I, int E,
                 int k, int e0, int E_local, int renormalize, moe_bf16* y, void* workspace,
                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_forward whose share y [T, H] is float32 (the partial-output form of
+ * moe_combine_f32, same citation): every step is moe_forward's, only the
+ * combine stores its float32 sums unrounded. Rounding y to bf16 gives
+ * moe_forward's y bit for bit; the float32 shares of ranks that split
+ * [0, E) add up to the whole layer with one rounding. Workspace and checks
+ * are moe_forward's.
+ */
+int moe_forward_f32(const moe_bf16* x, const float* w_router, const float* bias,
+                    const moe_bf16* w_gate_up, const moe_bf16* w_down, int T, int H, int I, int E,
+                    int k, int e0, int E_local, int renormalize, float* y, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
 
 /*
  * moe_forward with timing marks: records events[0..5] on `stream` before the

@@ -19,7 +19,7 @@ FAKE_ODD = ctypes.c_void_p(0x10002)  # not 16-byte aligned
 def header_functions():
     text = HEADER.read_text()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(moe_[a-z_]+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(moe_[a-z_0-9]+)\s*\(", text, flags=re.M)))
 
 
 def test_library_exports_every_header_symbol():
@@ -130,16 +130,17 @@ def test_expert_ffn_rejects(args, want):
     ((FAKE, FAKE, FAKE, 4, 8, 1, FAKE_ODD, None), M.MOE_ERR_INVALID_ARG),
     ((None, None, None, 0, 8, 1, None, None), M.MOE_OK),
 ])
-def test_combine_rejects(args, want):
-    assert M.lib().moe_combine(*args) == want
+@pytest.mark.parametrize("name", ["moe_combine", "moe_combine_f32"])
+def test_combine_rejects(name, args, want):
+    assert getattr(M.lib(), name)(*args) == want
 
 
-def _forward(**kw):
+def _forward(name="moe_forward", **kw):
     a = dict(x=FAKE, w=FAKE, b=None, gu=FAKE, d=FAKE, T=8, H=8, I=8, E=4, k=2, e0=0, El=4, renorm=1, y=FAKE,
              ws=ctypes.c_void_p(0x100000), wsb=1 << 30)
     a.update(kw)
-    return M.lib().moe_forward(a["x"], a["w"], a["b"], a["gu"], a["d"], a["T"], a["H"], a["I"], a["E"], a["k"],
-                               a["e0"], a["El"], a["renorm"], a["y"], a["ws"], a["wsb"], None)
+    return getattr(M.lib(), name)(a["x"], a["w"], a["b"], a["gu"], a["d"], a["T"], a["H"], a["I"], a["E"],
+                                  a["k"], a["e0"], a["El"], a["renorm"], a["y"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -155,5 +156,6 @@ def _forward(**kw):
     (dict(k=0), M.MOE_ERR_INVALID_ARG),
     (dict(T=0, x=None, y=None), M.MOE_OK),
 ])
-def test_forward_rejects(kw, want):
-    assert _forward(**kw) == want
+@pytest.mark.parametrize("name", ["moe_forward", "moe_forward_f32"])
+def test_forward_rejects(name, kw, want):
+    assert _forward(name, **kw) == want
