@@ -51,9 +51,45 @@ combine_kernel(const uint16_t* __restrict__ expert_out, const int32_t* __restric
   // Start from -0 so that a single term passes through bit for bit (-0 + -0 = -0);
   // a token with no local slot is written as +0.
   const float init = nl > 0 ? -0.f : 0.f;
+  if constexpr (F32) {
+    // 4 values per lane and vector, so each store instruction covers one
+    // contiguous 1 KiB span of y; the stores are non-temporal (y is twice the
+    // bytes of the bf16 form and is not read again here). With bf16 output,
+    // non-temporal stores measured slower, so that path keeps plain ones.
+    const int nv = H / 4;
+    f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(y) + int64_t(t) * H);
+    constexpr int U = 4;
+    for (int v0 = lane; v0 < nv; v0 += 64 * U) {
+      u32x2 q[KMAX][U];
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (j < nl && v0 + 64 * u < nv)
+            q[j][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(expert_out + int64_t(rows[j]) * H) + v0 + 64 * u);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (v0 + 64 * u >= nv) break;
+        float acc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = init;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+          if (j < nl) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              acc[2 * i] = fmaf(wts[j], bf16_lo(q[j][u][i]), acc[2 * i]);
+              acc[2 * i + 1] = fmaf(wts[j], bf16_hi(q[j][u][i]), acc[2 * i + 1]);
+            }
+          }
+        }
+        __builtin_nontemporal_store(f32x4{acc[0], acc[1], acc[2], acc[3]}, dst + v0 + 64 * u);
+      }
+    }
+    return;
+  }
   const int nv = H / 8;
   u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + int64_t(t) * H);
-  float4* dstf = reinterpret_cast<float4*>(static_cast<float*>(y) + int64_t(t) * H);
   // U vectors per lane per pass; all of a pass's loads are issued before the
   // first one is used, so each lane keeps up to U * nl loads in flight.
   constexpr int U = 2;
@@ -81,16 +117,10 @@ combine_kernel(const uint16_t* __restrict__ expert_out, const int32_t* __restric
           }
         }
       }
-      if constexpr (F32) {
-        const int v = v0 + 64 * u;
-        dstf[2 * v] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        dstf[2 * v + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-      } else {
-        u32x4 o;
+      u32x4 o;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-        dst[v0 + 64 * u] = o;
-      }
+      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+      dst[v0 + 64 * u] = o;
     }
   }
 }

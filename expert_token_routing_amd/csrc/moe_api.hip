@@ -66,7 +66,7 @@ static ForwardLayout forward_layout(int T, int H, int I, int E, int k, int E_loc
     return at;
   };
   L.planes = take(size_t(3) * E * H * sizeof(uint16_t));
-  L.part = take(size_t(T) * E * sizeof(float));
+  L.part = take(size_t(route_k_parts(T, H, E) - 1) * T * E * sizeof(float));
   L.logits = take(size_t(T) * E * sizeof(float));
   L.topk_idx = take(size_t(T) * k * sizeof(int32_t));
   L.topk_w = take(size_t(T) * k * sizeof(float));
@@ -102,7 +102,8 @@ const char* moe_status_string(int status) {
 size_t moe_route_workspace_size(int T, int H, int E, int k) {
   (void)k;
   if (H <= 0 || E <= 0 || T < 0) return 0;
-  return align_up(size_t(3) * E * H * sizeof(uint16_t)) + align_up(size_t(T) * E * sizeof(float));
+  return align_up(size_t(3) * E * H * sizeof(uint16_t)) +
+         align_up(size_t(route_k_parts(T, H, E) - 1) * T * E * sizeof(float));
 }
 
 int moe_route(const moe_bf16* x, const float* w_router, const float* bias, int T, int H, int E, int k,

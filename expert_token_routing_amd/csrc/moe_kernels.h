@@ -15,6 +15,10 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Router: planes must hold 3*E*H bf16.
 // planes: 3 x E x H bf16 scratch; part: T x E float32 scratch (second k half)
+// Parts the router's k range is split into (1: no split); the workspace holds
+// parts - 1 float32 [T, E] partials besides the logits.
+int route_k_parts(int T, int H, int E);
+
 hipError_t launch_route(const uint16_t* x, const float* w_router, const float* bias, int T, int H, int E, int k,
                         int renormalize, float* logits, int32_t* topk_idx, float* topk_w, uint16_t* planes, float* part,
                         hipStream_t stream);

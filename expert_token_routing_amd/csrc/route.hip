@@ -104,16 +104,18 @@ route_logits_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
 }
 
 // Same logits through the direct-to-LDS pipeline (H a multiple of 64), with
-// the k range split in two halves that run as separate workgroups
-// (blockIdx.z): tiles of 256 tokens x 128 experts per half, 8 waves of
+// the k range split into S parts that run as separate workgroups
+// (blockIdx.z): tiles of 256 tokens x 128 experts per part, 8 waves of
 // 64 x 64 (each token fragment read from LDS serves 2 x 3 products, each
 // weight fragment 2), so LDS reads per product are about a quarter lower than
-// with 128 x 128 tiles while there are still 256 workgroups for T = 16384,
-// E = 256. The token rows and the three weight planes come in 64-deep stages
-// (every request a whole 128-byte line) through two LDS buffers; stage s + 2
-// is issued right after the barrier at which every wave has finished reading
-// stage s. Half z writes its raw partial sums to out[z]; the top-k kernel
-// adds the two halves and the bias in a fixed order.
+// with 128 x 128 tiles. S is 2 when the tiles alone fill the chip (T = 16384,
+// E = 256: 256 workgroups) and grows as T shrinks, down to 4 stages per part
+// (a decode step of 256 tokens: 28 parts). The token rows and the three
+// weight planes come in 64-deep stages (every request a whole 128-byte line)
+// through two LDS buffers; stage s + 2 is issued right after the barrier at
+// which every wave has finished reading stage s. Part z writes its raw
+// partial sums to out0 (z = 0) or out1 + (z - 1) T E; the top-k kernel adds
+// the parts in order, then the bias.
 namespace routedma {
 
 constexpr int kBM = 256, kBN = 128, kFM = 2, kFN = 2, kPlanes = 3;
@@ -125,7 +127,7 @@ constexpr int kBufs = 2;
 
 __global__ void __launch_bounds__(dma::kThreads)
 route_logits_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes, float* __restrict__ out0,
-                        float* __restrict__ out1, int T, int H, int E) {
+                        float* __restrict__ out1, int T, int H, int E, int per) {
   using namespace dma;
   __shared__ __attribute__((aligned(1024))) char smem[kBufs * kStage];
   MOE_LDS char* lds = (MOE_LDS char*)smem;
@@ -134,11 +136,10 @@ route_logits_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
   const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
   const int lane = lane_id();
   const int nk_all = H / kSK;
-  const int half = (nk_all + 1) / 2;
-  const int s0 = blockIdx.z * half;
-  const int nk = max(0, min(nk_all, s0 + half) - s0);  // stages of this half
+  const int s0 = blockIdx.z * per;
+  const int nk = max(0, min(nk_all, s0 + per) - s0);  // stages of this part
   const int64_t plane = int64_t(E) * H;
-  float* __restrict__ out = blockIdx.z == 0 ? out0 : out1;
+  float* __restrict__ out = blockIdx.z == 0 ? out0 : out1 + int64_t(blockIdx.z - 1) * T * E;
 
   RowLoader64<kBM> la;
   RowLoader64<kBN> lb[kPlanes];
@@ -261,8 +262,8 @@ route_logits_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
 // LDS) and then the lowest expert id holding it (one ballot per EPL slot).
 template <int EPL>
 __global__ void __launch_bounds__(kThreads)
-route_topk_kernel(float* __restrict__ logits, const float* __restrict__ part, const float* __restrict__ bias, int T,
-                  int E, int k, int renormalize, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+route_topk_kernel(float* __restrict__ logits, const float* __restrict__ part, int nparts, const float* __restrict__ bias,
+                  int T, int E, int k, int renormalize, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
   const int lane = lane_id();
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -270,13 +271,16 @@ route_topk_kernel(float* __restrict__ logits, const float* __restrict__ part, co
   float v[EPL];
   uint32_t live = 0;  // bit i: expert lane + 64 i exists and is not taken yet
   float lm = -INFINITY;
-  if (part != nullptr) {  // logits hold the first k half: add the second, then the bias; store the sum
+  if (part != nullptr) {  // logits hold the first k part: add the others in order, then the bias; store the sum
     const float* prow = part + int64_t(t) * E;
+    const int64_t pstride = int64_t(T) * E;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = lane + 64 * i;
       if (e < E) {
-        const float l = (row[e] + prow[e]) + (bias != nullptr ? bias[e] : 0.f);
+        float l = row[e];
+        for (int z = 0; z < nparts; ++z) l += prow[z * pstride + e];
+        l += bias != nullptr ? bias[e] : 0.f;
         row[e] = l;
         v[i] = l;
       }
@@ -338,6 +342,20 @@ route_topk_kernel(float* __restrict__ logits, const float* __restrict__ part, co
 // ---------------------------------------------------------------------------
 // Host-side launchers
 // ---------------------------------------------------------------------------
+int route_k_parts(int T, int H, int E) {
+  if (H % routedma::kSK != 0) return 1;
+  const int nk_all = H / routedma::kSK;
+  const int64_t tiles = int64_t((T + routedma::kBM - 1) / routedma::kBM) * ((E + routedma::kBN - 1) / routedma::kBN);
+  // enough parts for about 256 workgroups, at least 2, each part at least 4
+  // stages deep; then as few parts as that depth needs
+  int64_t want = std::max<int64_t>(2, (256 + tiles - 1) / std::max<int64_t>(tiles, 1));
+  want = std::min<int64_t>(want, std::max(2, nk_all / 4));
+  want = std::min<int64_t>(want, nk_all);
+  if (want < 2) return 1;
+  const int per = int((nk_all + want - 1) / want);
+  return (nk_all + per - 1) / per;
+}
+
 hipError_t launch_route(const uint16_t* x, const float* w_router, const float* bias, int T, int H, int E, int k,
                         int renormalize, float* logits, int32_t* topk_idx, float* topk_w, uint16_t* planes, float* part,
                         hipStream_t stream) {
@@ -349,13 +367,16 @@ hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  const bool split = H % routedma::kSK == 0;
+  const int parts = route_k_parts(T, H, E);
+  const bool split = parts > 1;
   {
     if (split) {
+      const int nk_all = H / routedma::kSK;
+      const int per = (nk_all + parts - 1) / parts;
       dim3 grid(unsigned((T + routedma::kBM - 1) / routedma::kBM), unsigned((E + routedma::kBN - 1) / routedma::kBN),
-                2u);
+                unsigned(parts));
       hipLaunchKernelGGL(routedma::route_logits_dma_kernel, grid, dim3(dma::kThreads), 0, stream, x, planes, logits,
-                         part, T, H, E);
+                         part, T, H, E, per);
     } else {
       dim3 grid(unsigned((T + 127) / 128), unsigned((E + 127) / 128));
       hipLaunchKernelGGL(route_logits_kernel, grid, dim3(kThreads), 0, stream, x, planes, bias, logits, T, H, E);
@@ -368,8 +389,8 @@ hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b
     dim3 grid(unsigned((T + 3) / 4));
     const int epl = (E + 63) / 64;
 #define MOE_TOPK_LAUNCH(EPL)                                                                                       \
-  hipLaunchKernelGGL(route_topk_kernel<EPL>, grid, dim3(kThreads), 0, stream, logits, pt, bias, T, E, k, renormalize, \
-                     topk_idx, topk_w)
+  hipLaunchKernelGGL(route_topk_kernel<EPL>, grid, dim3(kThreads), 0, stream, logits, pt, parts - 1, bias, T, E, k, \
+                     renormalize, topk_idx, topk_w)
     if (epl <= 1)
       MOE_TOPK_LAUNCH(1);
     else if (epl <= 2)

@@ -68,9 +68,10 @@ const char* moe_status_string(int status);
 /* Router: logits, top-k selection and combine weights.                      */
 /* ------------------------------------------------------------------------ */
 
-/* Bytes of device workspace moe_route needs (a bfloat16 three-way split of
- * the float32 router weight, and float32 partial logits of one half of the
- * hidden dimension). */
+/* Bytes of device workspace moe_route needs: a bfloat16 three-way split of
+ * the float32 router weight, and float32 [T, E] partial logits for all but one
+ * of the parts the hidden dimension is split into (2 parts when the token
+ * count alone fills the GPU, more for few tokens). */
 size_t moe_route_workspace_size(int T, int H, int E, int k);
 
 /*

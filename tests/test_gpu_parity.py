@@ -56,6 +56,9 @@ SMALL_CASES = [
     ragged("dma_wide_n", T=640, H=576, I=448, E=16, k=4, e0=3, E_local=6, renormalize=0),
     # k extents that end in half a 64-deep stage (H % 64 == I % 64 == 32)
     ragged("dma_half_stage", T=700, H=160, I=224, E=8, k=2, e0=2, E_local=4),
+    # few tokens for a long hidden dimension: the router's k range in 4 parts
+    # (19 stages of 64: 5 + 5 + 5 + 4)
+    ragged("route_parts", T=200, H=1216, I=96, E=40, k=4, e0=8, E_local=8),
 ]
 
 
@@ -179,18 +182,19 @@ def check_combine(cfg, res, gw, rinv):
 # --------------------------------------------------------------------------- #
 # tests                                                                        #
 # --------------------------------------------------------------------------- #
-def test_mfma_router_split_is_exact():
+@pytest.mark.parametrize("T,H,E", [(192, 136, 70), (192, 1216, 70), (100, 7168, 256)])
+def test_mfma_router_split_is_exact(T, H, E):
     """One-hot tokens make each logit a single product x*w = w, so the three
-    bf16 parts must add back to the float32 router weight exactly."""
+    bf16 parts must add back to the float32 router weight exactly (and every
+    other k part of a split sum adds zeros)."""
     dev = device()
     rng = np.random.default_rng(5)
-    T, H, E = 192, 136, 70
     xf = np.zeros((T, H), np.float32)
     hsel = rng.integers(0, H, size=T)
     xf[np.arange(T), hsel] = 1.0
     x = W.bf16_bits_from_f32(xf)
     wr = (rng.standard_normal((E, H)) * np.exp(rng.uniform(-20, 20, (E, H)))).astype(np.float32)
-    say("moe_route split exactness T=192 H=136 E=70")
+    say(f"moe_route split exactness T={T} H={H} E={E}")
     logits, idx, w = M.moe_route(to_dev_bf16(x, dev), to_dev(wr, dev), None, 3, True)
     gl = logits.cpu().numpy()
     assert np.array_equal(gl, wr[:, hsel].T), np.argwhere(gl != wr[:, hsel].T)[:4]
@@ -373,7 +377,8 @@ def test_empty_batch_is_noop():
 # --------------------------------------------------------------------------- #
 # the named workloads at their full sizes                                       #
 # --------------------------------------------------------------------------- #
-@pytest.mark.parametrize("name", ["small_top2", "gptoss20b_ep8_share", "dsr1_ep8_share", "dsr1_ep8_share_zipf"])
+@pytest.mark.parametrize("name", ["small_top2", "gptoss20b_ep8_share", "dsr1_ep8_share", "dsr1_ep8_decode",
+                                  "dsr1_ep8_share_zipf"])
 def test_named_workload_full_size(name):
     cfg = W.CONFIGS[name]
     dev = device()
