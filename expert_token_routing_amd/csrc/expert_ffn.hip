@@ -209,8 +209,10 @@ __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __re
   const int nk = (K + kSK - 1) / kSK;
   const bool half_tail = (K % kSK) != 0;
   const int r16 = (rows + 15) & ~15;
+  constexpr int kAStage = a_stage_bytes(FMT);
+  constexpr int kStages = stages_for(FMT);
   MOE_LDS char* const ldsA = lds;
-  MOE_LDS char* const ldsB = lds + dma::panel::kStages * kAStage;
+  MOE_LDS char* const ldsB = lds + kStages * kAStage;
 
   f32x4v acc[FMT][kFN];
 #pragma unroll
@@ -225,7 +227,7 @@ __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __re
   const int nl = la.count + BLoaderP::kPer;  // DMA instructions of this wave per stage
   auto issue = [&](int st) {
     if (st < nk) {
-      const int buf = st % dma::panel::kStages;
+      const int buf = st % kStages;
       la.issue(ldsA + buf * kAStage, st * kSK);
       lb.issue(ldsB + buf * kBStage, st);
     }
@@ -234,14 +236,14 @@ __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __re
   // the ones issued after s (s+1 .. min(last, nk-1)) may stay in flight.
   auto wait_stage = [&](int s, int last) {
     const int ahead = max(0, min(last, nk - 1) - s);
-    dma::wait_vm_barrier_dyn<(dma::panel::kStages - 1) * (ALoaderP::kPerMax + BLoaderP::kPer)>(ahead * nl);
+    dma::wait_vm_barrier_dyn<(kStages - 1) * (ALoaderP::kPerMax + BLoaderP::kPer)>(ahead * nl);
   };
   FragAddrP fa;
   fa.init(wm, wn);
   u32x4 a[FMT], b[kFN];
 
-  for (int st = 0; st < dma::panel::kStages; ++st) issue(st);
-  wait_stage(0, dma::panel::kStages - 1);
+  for (int st = 0; st < kStages; ++st) issue(st);
+  wait_stage(0, kStages - 1);
 #pragma unroll
   for (int j = 0; j < kFN; ++j) b[j] = read_b<0>(ldsB, fa, j);
 #pragma unroll
@@ -252,7 +254,7 @@ __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __re
     if constexpr (kSub == 2) {
       // k step 0 of stage kt; step 1's fragments (same buffer, landed) stream
       // in behind it, each A row right after its last use
-      const int cb = kt % dma::panel::kStages;
+      const int cb = kt % kStages;
       const MOE_LDS char* cA = ldsA + cb * kAStage;
       const MOE_LDS char* cB = ldsB + cb * kBStage;
       u32x4 bs[kFN];
@@ -285,9 +287,9 @@ __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __re
     // kt+1 landed: refill stage kt's buffer with stage kt+kStages, read stage kt+1
     dma::wait_lgkm0();
     // stages issued so far: up to kt + kStages - 1
-    if (kt + 1 < nk) wait_stage(kt + 1, kt + dma::panel::kStages - 1); else dma::wait_vm_barrier<0>();
-    issue(kt + dma::panel::kStages);
-    const int nb = (kt + 1) % dma::panel::kStages;
+    if (kt + 1 < nk) wait_stage(kt + 1, kt + kStages - 1); else dma::wait_vm_barrier<0>();
+    issue(kt + kStages);
+    const int nb = (kt + 1) % kStages;
     const MOE_LDS char* nA = ldsA + nb * kAStage;
     const MOE_LDS char* nB = ldsB + nb * kBStage;
     u32x4 bn[kFN];

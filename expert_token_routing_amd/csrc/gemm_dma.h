@@ -190,11 +190,29 @@ constexpr int kSub = kSK / 32;               // MFMA k steps per stage
 constexpr int kRowBytes = kSK * 2;           // bytes of one A row in a stage (64 or 128)
 constexpr int kLanesPerRow = kRowBytes / 16; // 4 or 8
 constexpr int kRowsPerLoad = 64 / kLanesPerRow;
-constexpr int kAStage = kRowsMax * kRowBytes;
 constexpr int kBStage = kSK * kBN * 2;
-constexpr int kStages = (160 * 1024 - 2048) / (kAStage + kBStage) >= 4 ? 4 : (160 * 1024 - 2048) / (kAStage + kBStage);
-constexpr int kLdsBytes = kStages * (kAStage + kBStage);
-static_assert(kStages >= 2, "two stages must fit in LDS");
+// Pipeline depth by tile height: a tile of FMT fragments per wave row has an
+// A stage of 16 kWR FMT rows, and gets 4 stages when 4 fit in the LDS left
+// beside the tile schedule's tables (about 8 KiB), else 2. Only FMT = 1 tiles
+// (up to 32 rows: few rows per expert, where the weight stream is the whole
+// cost) get 4, keeping twice the weight bytes in flight. A depth of 3 would
+// fit up to FMT = 4, but the buffer rotation modulo 3 made the kernel spill
+// registers.
+constexpr int kLdsBudget = 160 * 1024 - 8 * 1024 - 512;
+constexpr int a_stage_bytes(int fmt) { return 16 * kWR * fmt * kRowBytes; }
+constexpr int stages_for(int fmt) {
+  return kLdsBudget / (a_stage_bytes(fmt) + kBStage) >= 4 ? 4 : 2;
+}
+constexpr int lds_bytes_max() {
+  int m = 0;
+  for (int f = 1; f <= kFMMax; ++f) {
+    const int b = stages_for(f) * (a_stage_bytes(f) + kBStage);
+    m = b > m ? b : m;
+  }
+  return m;
+}
+constexpr int kLdsBytes = lds_bytes_max();
+static_assert(2 * (a_stage_bytes(kFMMax) + kBStage) <= kLdsBudget, "two stages of the tallest tile must fit in LDS");
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 

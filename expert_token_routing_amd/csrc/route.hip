@@ -274,15 +274,35 @@ route_topk_kernel(float* __restrict__ logits, const float* __restrict__ part, in
   if (part != nullptr) {  // logits hold the first k part: add the others in order, then the bias; store the sum
     const float* prow = part + int64_t(t) * E;
     const int64_t pstride = int64_t(T) * E;
+    float l[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      l[i] = e < E ? row[e] : 0.f;
+    }
+    // eight parts' loads in flight at a time, added in part order
+    for (int z0 = 0; z0 < nparts; z0 += 8) {
+      float pv[8][EPL];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+          const int e = lane + 64 * i;
+          pv[u][i] = (z0 + u < nparts && e < E) ? prow[(z0 + u) * pstride + e] : 0.f;
+        }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (z0 + u < nparts)
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) l[i] += pv[u][i];
+    }
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = lane + 64 * i;
       if (e < E) {
-        float l = row[e];
-        for (int z = 0; z < nparts; ++z) l += prow[z * pstride + e];
-        l += bias != nullptr ? bias[e] : 0.f;
-        row[e] = l;
-        v[i] = l;
+        const float b = l[i] + (bias != nullptr ? bias[e] : 0.f);
+        row[e] = b;
+        v[i] = b;
       }
     }
   }
