@@ -137,18 +137,21 @@ def summarize_counters(fetch_dir, write_dir, command):
     return "\n".join(lines) + "\n"
 
 
-def algorithmic(cfg, N, U, fused_gather=True):
-    """Algorithmic work of each stage for realised local rows N and source
-    tokens with a local pick U. In the fused forward, dispatch only builds the
-    tables (GEMM1 reads the token rows in place); the row-moving dispatch of
-    the standalone entry point is `dispatch_rows`."""
+def algorithmic(cfg, N, U, E_hit, fused_gather=True):
+    """Algorithmic work of each stage for realised local rows N, source
+    tokens with a local pick U and local experts with at least one row E_hit.
+    In the fused forward, dispatch only builds the tables (GEMM1 reads the
+    token rows in place); the row-moving dispatch of the standalone entry
+    point is `dispatch_rows`. GEMM bytes: every weight of a used expert once,
+    the input rows once, the output rows once."""
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
     rows = dict(bytes=2.0 * U * H + 2.0 * N * H + 8.0 * T * k + 4.0 * N)
     return {
         "route": dict(flop=2.0 * T * E * H, bytes=2.0 * T * H + 4.0 * E * H + 4.0 * T * E + 8.0 * T * k),
         "dispatch": dict(bytes=8.0 * T * k + 4.0 * N) if fused_gather else rows,
-        "gemm1_gate_up_swiglu": dict(flop=4.0 * N * H * I),
-        "gemm2_down": dict(flop=2.0 * N * I * H),
+        "gemm1_gate_up_swiglu": dict(flop=4.0 * N * H * I,
+                                     bytes=4.0 * E_hit * H * I + 2.0 * (U if fused_gather else N) * H + 2.0 * N * I),
+        "gemm2_down": dict(flop=2.0 * N * I * H, bytes=2.0 * E_hit * I * H + 2.0 * N * I + 2.0 * N * H),
         "combine": dict(bytes=2.0 * N * H + 2.0 * T * H + 8.0 * T * k),
         "dispatch_rows": rows,
     }
@@ -377,7 +380,8 @@ def main():
     N = int(offs[-1])
     U = int((inv >= 0).any(1).sum())
     fused = cfg.H % 32 == 0 and cfg.T * cfg.H * 2 < 2 ** 31
-    work = algorithmic(cfg, N, U, fused)
+    E_hit = int((np.diff(offs) > 0).sum())
+    work = algorithmic(cfg, N, U, E_hit, fused)
 
     # the standalone dispatch entry point (tables + rows moved into x_perm),
     # timed on its own with the forward's top-k ids
@@ -436,6 +440,7 @@ def main():
             s["gbs"] = round(work[n]["bytes"] / (ms * 1e-3) / 1e9, 1)
         if n.startswith("gemm"):
             s["frac_mfma_bf16"] = round(s["tflops"] / PEAK_BF16_TFLOPS, 4)
+            s["frac_hbm"] = round(s["gbs"] / PEAK_HBM_GBS, 4)
         if n in ("dispatch", "combine"):
             s["frac_hbm"] = round(s["gbs"] / PEAK_HBM_GBS, 4)
         stages[n] = s
@@ -445,8 +450,25 @@ def main():
     dispatch_rows = {"us": round(d_ms * 1e3, 2), "gbs": round(d_gbs, 1), "frac_hbm": round(d_gbs / PEAK_HBM_GBS, 4),
                      "note": "moe_dispatch entry point (tables + token rows copied to x_perm), timed alone"}
 
-    g1 = work["gemm1_gate_up_swiglu"]["flop"] / (stage_avg[2] * 1e-3) / 1e12
+    # GEMM1's bound from its arithmetic intensity: flop per algorithmic byte
+    # against the ridge point of the bf16 matrix peak and the HBM peak
+    w1 = work["gemm1_gate_up_swiglu"]
+    intensity = w1["flop"] / w1["bytes"]
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    g1 = w1["flop"] / (stage_avg[2] * 1e-3) / 1e12
+    g1_gbs = w1["bytes"] / (stage_avg[2] * 1e-3) / 1e9
     traffic, traffic_note = recorded_gemm1_traffic() if cfg.name == "dsr1_ep8_share" else (None, "other workload")
+    if intensity >= ridge:
+        roofline = {"bound": "mfma", "kernel": "grouped GEMM1 (gate/up + SwiGLU)",
+                    "achieved": round(g1, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(g1 / PEAK_BF16_TFLOPS, 4)}
+    else:
+        roofline = {"bound": "hbm", "kernel": "grouped GEMM1 (gate/up + SwiGLU)",
+                    "achieved": round(g1_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(g1_gbs / PEAK_HBM_GBS, 4)}
+    roofline.update({"traffic": traffic, "traffic_unit": "HBM bytes per launch", "traffic_source": traffic_note,
+                     "intensity_flop_per_byte": round(intensity, 1), "ridge_flop_per_byte": round(ridge, 1),
+                     "algorithmic_bytes": w1["bytes"], "algorithmic_flop": w1["flop"]})
     gemm_ms = stage_avg[2] + stage_avg[3]
     gemm_tflops = 6.0 * N * cfg.H * cfg.I / (gemm_ms * 1e-3) / 1e12
     ms_per_step = wall / args.steps * 1e3
@@ -467,10 +489,7 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "k": cfg.k,
                    "e0": cfg.e0, "E_local": cfg.E_local, "renormalize": cfg.renormalize,
                    "parallelism": "one EP rank's share on 1 GPU"},
-        "roofline": {"bound": "mfma", "kernel": "grouped GEMM1 (gate/up + SwiGLU)",
-                     "achieved": round(g1, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(g1 / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "traffic_unit": "HBM bytes per launch", "traffic_source": traffic_note},
+        "roofline": roofline,
         "grouped_gemm": {"tflops": round(gemm_tflops, 2), "frac_mfma_bf16": round(gemm_tflops / PEAK_BF16_TFLOPS, 4)},
         "stages": stages,
         "dispatch_rows": dispatch_rows,

@@ -8,7 +8,8 @@
 // ranks gets zeros, so the ranks' outputs add up to the full layer ("Expert
 // Parallelism (EP)", "Why a Single All-Reduce/Reduce-Scatter Works").
 //
-// One wave per token; the sum runs in float32 over the slots in order and is
+// One wave per token (per column block of the token's row when there are few
+// tokens); the sum runs in float32 over the slots in order and is
 // rounded to bf16 once, or stored as float32 as it stands (the partial-output
 // form: the shares of all ranks are summed afterwards, and a float32 share is
 // not rounded before that sum). The expert rows are read with non-temporal
@@ -22,7 +23,7 @@ namespace moe {
 template <int KMAX, bool F32>
 __global__ void __launch_bounds__(kThreads)
 combine_kernel(const uint16_t* __restrict__ expert_out, const int32_t* __restrict__ inv,
-               const float* __restrict__ topk_w, int T, int H, int k, void* __restrict__ y) {
+               const float* __restrict__ topk_w, int T, int H, int k, int vpb, void* __restrict__ y) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int lane = lane_id();
@@ -56,10 +57,10 @@ combine_kernel(const uint16_t* __restrict__ expert_out, const int32_t* __restric
     // contiguous 1 KiB span of y; the stores are non-temporal (y is twice the
     // bytes of the bf16 form and is not read again here). With bf16 output,
     // non-temporal stores measured slower, so that path keeps plain ones.
-    const int nv = H / 4;
+    const int nv = min(H / 4, 2 * vpb * int(blockIdx.y + 1));
     f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(y) + int64_t(t) * H);
     constexpr int U = 4;
-    for (int v0 = lane; v0 < nv; v0 += 64 * U) {
+    for (int v0 = 2 * vpb * blockIdx.y + lane; v0 < nv; v0 += 64 * U) {
       u32x2 q[KMAX][U];
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
@@ -88,12 +89,12 @@ combine_kernel(const uint16_t* __restrict__ expert_out, const int32_t* __restric
     }
     return;
   }
-  const int nv = H / 8;
+  const int nv = min(H / 8, vpb * int(blockIdx.y + 1));
   u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + int64_t(t) * H);
   // U vectors per lane per pass; all of a pass's loads are issued before the
   // first one is used, so each lane keeps up to U * nl loads in flight.
   constexpr int U = 2;
-  for (int v0 = lane; v0 < nv; v0 += 64 * U) {
+  for (int v0 = vpb * blockIdx.y + lane; v0 < nv; v0 += 64 * U) {
     u32x4 q[KMAX][U];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
@@ -128,9 +129,16 @@ combine_kernel(const uint16_t* __restrict__ expert_out, const int32_t* __restric
 template <bool F32>
 static void launch_combine_t(const uint16_t* expert_out, const int32_t* inv, const float* topk_w, int T, int H,
                              int k, void* y, hipStream_t stream) {
-  const dim3 grid(unsigned(ceil_div(T, 4)));
-#define MOE_COMBINE_LAUNCH(KM) \
-  hipLaunchKernelGGL((combine_kernel<KM, F32>), grid, dim3(kThreads), 0, stream, expert_out, inv, topk_w, T, H, k, y)
+  // Few tokens: each token's row is cut into column blocks (blockIdx.y) of
+  // vpb 8-column vectors (a multiple of 64), so that about 4096 waves run;
+  // with many tokens one wave takes a whole row.
+  const int nv = H / 8;
+  const int64_t want = std::max<int64_t>(1, std::min<int64_t>(ceil_div(4096, T), ceil_div(nv, 128)));
+  const int vpb = int(ceil_div(ceil_div(nv, want), 64) * 64);
+  const dim3 grid(unsigned(ceil_div(T, 4)), unsigned(ceil_div(nv, vpb)));
+#define MOE_COMBINE_LAUNCH(KM)                                                                                     \
+  hipLaunchKernelGGL((combine_kernel<KM, F32>), grid, dim3(kThreads), 0, stream, expert_out, inv, topk_w, T, H, k, \
+                     vpb, y)
   if (k <= 1)
     MOE_COMBINE_LAUNCH(1);
   else if (k <= 2)

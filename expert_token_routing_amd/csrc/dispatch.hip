@@ -9,15 +9,17 @@
 // [e0, e0 + E_local) ("Expert Parallelism (EP)", "Limitations").
 //
 // Row order is deterministic: segment of expert e0+i first by i, inside a
-// segment by token. Four kernels, no host synchronisation:
+// segment by token. Up to 1024 tokens, one workgroup builds every table in
+// one launch (dispatch_small_kernel); above that, four kernels, no host
+// synchronisation:
 //   1. histogram: one wave per chunk of 64 tokens counts its selections of
 //      every expert with LDS atomics -> chunk_table[e][chunk];
 //   2. scan: one workgroup per expert turns its row of chunk_table into
 //      exclusive prefixes and writes counts[e];
 //   3. index: one wave per chunk gives every local selection its row
 //      (segment start + chunk prefix + rank among earlier lanes that picked
-//      the same expert, found with one ballot per distinct expert) and fills
-//      perm_src and inv;
+//      the same expert, a popcount of the 64-bit set of lanes that picked
+//      it) and fills perm_src and inv;
 //   4. copy: one wave per token reads the token vector once and writes it to
 //      each of its rows, with non-temporal stores (the rows are not read
 //      again soon, so they should not evict other data from the caches).
@@ -63,6 +65,41 @@ dispatch_scan_kernel(int32_t* __restrict__ chunk_table, int nchunks, int32_t* __
   if (threadIdx.x == 0) counts[e] = carry;
 }
 
+// Gives every local selection of this wave's 64 tokens its row: segment
+// start seg[i] of local expert i, plus chunk_base(i) (the expert's selections
+// in earlier chunks), plus the number of earlier lanes of this wave that
+// picked the same expert. That count comes from mask[i], a 64-bit set of the
+// lanes that picked local expert i (every lane ORs in its bit first), so all
+// lanes place their selections at once. Non-local slots get inv = -1.
+// mask must be zero for this wave's local experts on entry.
+template <int KMAX, typename ChunkBase>
+__device__ __forceinline__ void place_wave(const int (&ev)[KMAX], int k, bool valid, int t, int e0, int E_local,
+                                           const int* seg, ChunkBase chunk_base, unsigned long long* mask,
+                                           int32_t* __restrict__ perm_src, int32_t* __restrict__ inv) {
+  const int lane = lane_id();
+  const unsigned long long bit = 1ull << lane;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j)
+    if (j < k && valid && ev[j] >= e0 && ev[j] < e0 + E_local) atomicOr(&mask[ev[j] - e0], bit);
+  __builtin_amdgcn_wave_barrier();
+  const uint64_t lt = lanemask_lt();
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k && valid) {
+      const int e = ev[j];
+      const int64_t slot = int64_t(t) * k + j;
+      if (e >= e0 && e < e0 + E_local) {
+        const int i = e - e0;
+        const int row = seg[i] + chunk_base(i) + __popcll(mask[i] & lt);
+        perm_src[row] = int32_t(slot);
+        inv[slot] = row;
+      } else {
+        inv[slot] = -1;
+      }
+    }
+  }
+}
+
 template <int KMAX>
 __global__ void __launch_bounds__(kThreads)
 dispatch_index_kernel(const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ chunk_base,
@@ -70,6 +107,7 @@ dispatch_index_kernel(const int32_t* __restrict__ topk_idx, const int32_t* __res
                       int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src, int32_t* __restrict__ inv) {
   __shared__ int s_seg[1024 + 1];
   __shared__ int s_base[4][1024];
+  __shared__ unsigned long long s_mask[4][1024];
   __shared__ int s_tmp[4];
   const int wv = threadIdx.x >> 6;
   const int c = blockIdx.x * 4 + wv;
@@ -97,7 +135,10 @@ dispatch_index_kernel(const int32_t* __restrict__ topk_idx, const int32_t* __res
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int i = lane + 64 * q;
-    if (i < E_local) s_base[wv][i] = cb[q];
+    if (i < E_local) {
+      s_base[wv][i] = cb[q];
+      s_mask[wv][i] = 0ull;
+    }
   }
   // Segment starts: exclusive scan of the local experts' counts.
   int sum = cnt[0] + cnt[1] + cnt[2] + cnt[3];
@@ -115,38 +156,78 @@ dispatch_index_kernel(const int32_t* __restrict__ topk_idx, const int32_t* __res
     for (int i = threadIdx.x; i <= E_local; i += kThreads) offsets[i] = s_seg[i];
 
   if (c >= nchunks) return;
-  uint32_t pend = 0;
+  place_wave<KMAX>(ev, k, valid, t, e0, E_local, s_seg, [&](int i) { return s_base[wv][i]; }, s_mask[wv], perm_src,
+                   inv);
+}
+
+// Whole dispatch table build in one workgroup for T <= kSmallTokens: wave w
+// takes chunk w, and every lane ORs its bit into s_mask[w][e] for each of its
+// experts. Popcounts of those sets give each chunk's count of every expert
+// (counts, and the local segment starts by a scan), the selections of an
+// expert in earlier chunks, and the rank among earlier lanes of the chunk:
+// the rows are the multi-kernel path's, bit for bit. One launch instead of
+// three: for a decode step the three launches cost more than their work.
+constexpr int kSmallWaves = 16;
+constexpr int kSmallTokens = kSmallWaves * kChunk;
+
+template <int KMAX>
+__global__ void __launch_bounds__(kSmallWaves * 64)
+dispatch_small_kernel(const int32_t* __restrict__ topk_idx, int T, int E, int k, int e0, int E_local,
+                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
+                      int32_t* __restrict__ inv) {
+  __shared__ unsigned long long s_mask[kSmallWaves][1024];  // lanes of chunk w that picked expert e
+  __shared__ int s_cnt[1024];
+  __shared__ int s_seg[1024 + 1];
+  __shared__ int s_tmp[kSmallWaves];
+  const int wv = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const int t = wv * kChunk + lane;
+  const bool valid = t < T;
+  const int nw = int((T + kChunk - 1) / kChunk);  // chunks holding tokens
+  int ev[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) ev[j] = (j < k && valid) ? topk_idx[int64_t(t) * k + j] : -1;
+  for (int e = lane; e < E; e += 64) s_mask[wv][e] = 0ull;
+  __syncthreads();
+  const unsigned long long bit = 1ull << lane;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j)
+    if (j < k && valid) atomicOr(&s_mask[wv][ev[j]], bit);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kSmallWaves * 64) {
+    int run = 0;
+    for (int w = 0; w < nw; ++w) run += __popcll(s_mask[w][e]);
+    counts[e] = run;
+    if (e >= e0 && e < e0 + E_local) s_cnt[e - e0] = run;
+  }
+  __syncthreads();
+  const int c = int(threadIdx.x) < E_local ? s_cnt[threadIdx.x] : 0;
+  int tot;
+  const int pre = block_exclusive_scan<kSmallWaves * 64>(c, s_tmp, tot);
+  if (int(threadIdx.x) < E_local) {
+    s_seg[threadIdx.x] = pre;
+    offsets[threadIdx.x] = pre;
+  }
+  if (threadIdx.x == 0) {
+    s_seg[E_local] = tot;
+    offsets[E_local] = tot;
+  }
+  __syncthreads();
+  if (!valid) return;
+  const uint64_t lt = lanemask_lt();
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
-    if (j < k && valid) {
+    if (j < k) {
       const int e = ev[j];
-      if (e >= e0 && e < e0 + E_local)
-        pend |= 1u << j;
-      else
-        inv[int64_t(t) * k + j] = -1;
-    }
-  }
-  while (true) {
-    const uint64_t active = ballot(pend != 0);
-    if (active == 0) break;
-    const int leader = __ffsll((unsigned long long)active) - 1;
-    int first = -1;
-#pragma unroll
-    for (int j = KMAX - 1; j >= 0; --j)
-      if ((pend >> j) & 1u) first = ev[j];
-    const int e_lead = __builtin_amdgcn_readlane(first, leader);
-    int js = -1;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-      if (((pend >> j) & 1u) && ev[j] == e_lead) js = j;
-    const uint64_t mask = ballot(js >= 0);
-    if (js >= 0) {
-      const int rank = __popcll(mask & lanemask_lt());
-      const int row = s_seg[e_lead - e0] + s_base[wv][e_lead - e0] + rank;
-      const int64_t slot = int64_t(t) * k + js;
-      perm_src[row] = int32_t(slot);
-      inv[slot] = row;
-      pend &= ~(1u << js);
+      const int64_t slot = int64_t(t) * k + j;
+      if (e >= e0 && e < e0 + E_local) {
+        int row = s_seg[e - e0] + __popcll(s_mask[wv][e] & lt);
+        for (int w = 0; w < wv; ++w) row += __popcll(s_mask[w][e]);
+        perm_src[row] = int32_t(slot);
+        inv[slot] = row;
+      } else {
+        inv[slot] = -1;
+      }
     }
   }
 }
@@ -189,6 +270,25 @@ dispatch_copy_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__
 hipError_t launch_dispatch_index(const int32_t* topk_idx, int T, int E, int k, int e0, int E_local, int32_t* counts,
                                  int32_t* offsets, int32_t* perm_src, int32_t* inv, int32_t* chunk_table,
                                  hipStream_t stream) {
+  if (T <= kSmallTokens) {
+#define MOE_SMALL_LAUNCH(KM)                                                                                  \
+  hipLaunchKernelGGL(dispatch_small_kernel<KM>, dim3(1), dim3(kSmallWaves * 64), 0, stream, topk_idx, T, E, k, \
+                     e0, E_local, counts, offsets, perm_src, inv)
+    if (k <= 1)
+      MOE_SMALL_LAUNCH(1);
+    else if (k <= 2)
+      MOE_SMALL_LAUNCH(2);
+    else if (k <= 4)
+      MOE_SMALL_LAUNCH(4);
+    else if (k <= 8)
+      MOE_SMALL_LAUNCH(8);
+    else if (k <= 16)
+      MOE_SMALL_LAUNCH(16);
+    else
+      MOE_SMALL_LAUNCH(32);
+#undef MOE_SMALL_LAUNCH
+    return hipGetLastError();
+  }
   const int nchunks = int(ceil_div(T, kChunk));
   const unsigned wgs = unsigned(ceil_div(nchunks, 4));
   hipLaunchKernelGGL(dispatch_hist_kernel, dim3(wgs), dim3(kThreads), size_t(4) * E * sizeof(int), stream,

@@ -46,6 +46,8 @@ CASES = [
     W.MoEConfig("f32_many_experts", T=257, H=136, I=72, E=1024, k=32, e0=512, E_local=96),
     W.MoEConfig("f32_dma", T=640, H=576, I=448, E=16, k=4, e0=3, E_local=6, renormalize=0),
     W.MoEConfig("f32_single_expert", T=129, H=72, I=24, E=7, k=7, e0=6, E_local=1),
+    # few tokens, long rows: each token's row is combined in two column blocks
+    W.MoEConfig("f32_col_blocks", T=100, H=2048, I=64, E=8, k=2, e0=0, E_local=8),
 ]
 
 
