@@ -351,6 +351,29 @@ def pin_sum_of_shares():
         assert np.allclose(tot, full, rtol=1e-12, atol=1e-14)
 
 
+def pin_sum_of_ep_tp_shares():
+    """Variable EP + TP: rank (r_ep, r_tp) holds experts [r_ep E_L, (r_ep+1) E_L)
+    with intermediate slice r_tp of tp (gate and up columns and down rows of
+    that slice, as the workload generator cuts them). Summing every rank's
+    output gives the layer with whole experts, all local ("Expert Parallelism
+    (EP)", "Variable EP (EP+TP for MoE)": one collective sums the TP partial
+    products and the EP expert contributions)."""
+    import workloads as W
+    full = W.MoEConfig("eptp_full", T=21, H=16, I=24, E=8, k=3, e0=0, E_local=8, x_scale=1.0)
+    fi = W.make_inputs(full)
+    y_full = O.oracle_forward(fi.x, fi.w_router, None, fi.w_gate_up, fi.w_down, 3, 0, 8, 1)
+    for ep, tp in [(1, 2), (2, 3), (4, 4), (8, 1)]:
+        El = 8 // ep
+        tot = np.zeros_like(y_full)
+        for r_ep in range(ep):
+            for r_tp in range(tp):
+                c = full.scaled(I=24 // tp, tp=tp, tp_rank=r_tp, e0=r_ep * El, E_local=El)
+                si = W.make_inputs(c)
+                assert si.w_gate_up.shape == (El, 16, 2 * (24 // tp))
+                tot += O.oracle_forward(si.x, si.w_router, None, si.w_gate_up, si.w_down, 3, c.e0, El, 1)
+        assert np.allclose(tot, y_full, rtol=1e-12, atol=1e-14), (ep, tp, float(np.max(np.abs(tot - y_full))))
+
+
 def pin_dense_equals_grouped():
     """The dispatch / grouped path equals the dense masked evaluation of every
     local expert on every token."""
@@ -386,6 +409,6 @@ def pin_bf16_decode():
 ALL_PINS = [
     pin_walkthrough_top1, pin_imbalance_top1, pin_top2_weighted_sum, pin_top4_partial_sums,
     pin_logits_bruteforce, pin_topk_bruteforce, pin_softmax_closed_form, pin_ffn_closed_form,
-    pin_ffn_hand_example, pin_dispatch_invariants, pin_identity_roundtrip, pin_sum_of_shares,
+    pin_ffn_hand_example, pin_dispatch_invariants, pin_identity_roundtrip, pin_sum_of_shares, pin_sum_of_ep_tp_shares,
     pin_dense_equals_grouped, pin_row_independence, pin_bf16_decode,
 ]

@@ -134,3 +134,38 @@ def test_ep_sweep_f32_shares_sum_to_layer():
         assert rel_max_err(tot, y_ref) <= OUT_TOL, ep
         # the layer rounded once is within the bar too
         assert rel_max_err(bf16_f64(torch.from_numpy(tot.astype(np.float32)).to(torch.bfloat16)), y_ref) <= OUT_TOL
+
+
+def test_ep_tp_shares_sum_to_layer():
+    """Variable EP + TP ("Expert Parallelism (EP)", "Variable EP (EP+TP for
+    MoE)"): rank (r_ep, r_tp) runs its local experts' intermediate slice r_tp
+    of tp. Each rank's float32 output meets the output bar against the
+    oracle's output for the same shard, and the sum over all ranks meets it
+    against the oracle's whole layer. Slices of 24 columns (tp = 16) take the
+    k-by-32 GEMM path, the others the panel path."""
+    dev = device()
+    full = W.MoEConfig("eptp", T=300, H=256, I=384, E=8, k=2, e0=0, E_local=8)
+    fi = W.make_inputs(full)
+    fd = DevInputs(fi, dev)
+    say("ep x tp shares: route T=300 E=8 k=2")
+    logits, _, _ = M.moe_route(fd.x, fd.w_router, fd.bias, full.k, full.renormalize)
+    gl = logits.cpu().numpy().astype(np.float64)
+    y_ref = O.oracle_forward(fi.x, fi.w_router, fi.bias, fi.w_gate_up, fi.w_down, full.k, 0, full.E,
+                             full.renormalize, logits=gl)
+    for ep, tp in [(1, 2), (2, 4), (4, 3), (2, 16)]:
+        El = full.E // ep
+        tot = np.zeros((full.T, full.H), np.float64)
+        for r_ep in range(ep):
+            for r_tp in range(tp):
+                c = full.scaled(I=full.I // tp, tp=tp, tp_rank=r_tp, e0=r_ep * El, E_local=El)
+                si = W.make_inputs(c)
+                sd = DevInputs(si, dev)
+                say(f"ep x tp shares: ep={ep} tp={tp} rank ({r_ep}, {r_tp}) I={c.I}")
+                y_r, _ = M.moe_forward_f32(sd.x, sd.w_router, sd.bias, sd.w_gate_up, sd.w_down, c.k, c.e0,
+                                           c.renormalize)
+                yr = y_r.cpu().numpy().astype(np.float64)
+                ref_r = O.oracle_forward(si.x, si.w_router, si.bias, si.w_gate_up, si.w_down, c.k, c.e0, El,
+                                         c.renormalize, logits=gl)
+                assert rel_max_err(yr, ref_r) <= OUT_TOL, (ep, tp, r_ep, r_tp)
+                tot += yr
+        assert rel_max_err(tot, y_ref) <= OUT_TOL, (ep, tp)

@@ -12,11 +12,21 @@ talk about:
   is ``[H, 2I]`` and ``down`` is ``[I, H]``, stacked with the expert index
   first; the router weight ``[E, H]`` is replicated and scores all experts;
   rank r owns the contiguous experts ``[r*E_L, (r+1)*E_L)`` ("Limitations").
-* The five configurations are a tiny top-1 case mirroring the walk-through of
+* The configurations are a tiny top-1 case mirroring the walk-through of
   "EP: Partition Experts and Route Tokens" (section "Send tokens to experts
   and return their results"), a small top-2 layer, a GPT-OSS-20B-shaped EP=8
-  rank share (32 experts, 4 local, top-4), a DeepSeek-R1-shaped EP=8 rank
-  share (256 experts, 32 local, top-8) and a skewed variant of the latter.
+  rank share (32 experts, 4 local, top-4), the same layer's EP=2 x TP=4 rank
+  share (16 local experts, a quarter of the intermediate dimension: "Expert
+  Parallelism (EP)", "Variable EP (EP+TP for MoE)" and the table of "How EP
+  Differs from TP for MoE"), a DeepSeek-R1-shaped EP=8 rank share (256
+  experts, 32 local, top-8), its decode-step size (256 tokens) and a skewed
+  variant.
+* Tensor-parallel shards (``tp > 1``): the experts are drawn at their full
+  intermediate size ``I * tp`` and rank ``tp_rank`` keeps intermediate
+  columns ``[tp_rank * I, (tp_rank + 1) * I)`` of both the gate half and the
+  up half of ``gate_up`` (stored gate slice first, then up slice, so the
+  shard has the ``[H, 2I]`` layout of a whole expert of size I) and the same
+  rows of ``down``.
 
 Generation recipe: numpy PCG64 with one substream per tensor and per expert,
 ``default_rng([seed, tensor_id, expert])``, float32 standard normal draws,
@@ -60,6 +70,8 @@ class MoEConfig:
     zipf_kappa: float = 1.0
     x_scale: float | None = None   # None: 1/sqrt(H)
     seed: int = 0
+    tp: int = 1                # > 1: the experts' intermediate dimension is I * tp; this share
+    tp_rank: int = 0           # holds slice tp_rank of it (I columns of gate, of up, I rows of down)
     note: str = ""
 
     @property
@@ -80,6 +92,10 @@ CONFIGS: dict[str, MoEConfig] = {
     "gptoss20b_ep8_share": MoEConfig("gptoss20b_ep8_share", T=8192, H=2880, I=3072, E=32, k=4,
                                      e0=0, E_local=4,
                                      note="GPT-OSS-20B-shaped layer, rank 0 of EP=8"),
+    "gptoss20b_ep2_tp4_share": MoEConfig("gptoss20b_ep2_tp4_share", T=8192, H=2880, I=768, E=32, k=4,
+                                         e0=0, E_local=16, tp=4, tp_rank=0,
+                                         note="GPT-OSS-20B-shaped layer, rank 0 of EP=2 x TP=4: 16 local "
+                                              "experts, intermediate slice 0 of 4"),
     "dsr1_ep8_share": MoEConfig("dsr1_ep8_share", T=16384, H=7168, I=2048, E=256, k=8,
                                 e0=0, E_local=32,
                                 note="DeepSeek-R1-shaped layer, rank 0 of EP=8"),
@@ -158,25 +174,29 @@ def make_inputs(cfg: MoEConfig, threads: int | None = None, weights: bool = True
     experts = list(range(cfg.e0, cfg.e0 + cfg.E_local))
     nthreads = threads or min(16, len(os.sched_getaffinity(0)))
 
-    def gu(e):
-        return _normal_bf16(cfg.seed, _TID_GATE_UP, e, (H, 2 * I), 1.0 / math.sqrt(H))
-
-    def dn(e):
-        return _normal_bf16(cfg.seed, _TID_DOWN, e, (I, H), 1.0 / math.sqrt(I))
+    def both(e):
+        return make_expert_weights(cfg, e)
 
     w_gu = np.empty((cfg.E_local, H, 2 * I), np.uint16)
     w_d = np.empty((cfg.E_local, I, H), np.uint16)
     with ThreadPoolExecutor(max(1, nthreads)) as ex:
-        for i, a in enumerate(ex.map(gu, experts)):
+        for i, (a, b) in enumerate(ex.map(both, experts)):
             w_gu[i] = a
-        for i, a in enumerate(ex.map(dn, experts)):
-            w_d[i] = a
+            w_d[i] = b
     return MoEInputs(cfg, x, wr, bias, w_gu, w_d)
 
 
 def make_expert_weights(cfg: MoEConfig, e: int) -> tuple[np.ndarray, np.ndarray]:
-    """gate_up [H, 2I] and down [I, H] of global expert ``e`` alone (same
-    values as ``make_inputs`` gives for that expert)."""
-    H, I = cfg.H, cfg.I
-    return (_normal_bf16(cfg.seed, _TID_GATE_UP, e, (H, 2 * I), 1.0 / math.sqrt(H)),
-            _normal_bf16(cfg.seed, _TID_DOWN, e, (I, H), 1.0 / math.sqrt(I)))
+    """gate_up [H, 2I] and down [I, H] of global expert ``e`` as this share
+    holds them (same values as ``make_inputs`` gives for that expert): the
+    whole expert, or its tensor-parallel slice ``tp_rank`` of ``tp``."""
+    H, I, tp, r = cfg.H, cfg.I, cfg.tp, cfg.tp_rank
+    if tp < 1 or not 0 <= r < tp:
+        raise ValueError(f"bad tensor-parallel shard {r} of {tp}")
+    If = I * tp
+    gu = _normal_bf16(cfg.seed, _TID_GATE_UP, e, (H, 2 * If), 1.0 / math.sqrt(H))
+    dn = _normal_bf16(cfg.seed, _TID_DOWN, e, (If, H), 1.0 / math.sqrt(If))
+    if tp == 1:
+        return gu, dn
+    cols = np.r_[r * I:(r + 1) * I, If + r * I:If + (r + 1) * I]
+    return np.ascontiguousarray(gu[:, cols]), np.ascontiguousarray(dn[r * I:(r + 1) * I])
