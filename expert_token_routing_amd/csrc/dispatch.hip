@@ -10,7 +10,8 @@
 //
 // Row order is deterministic: segment of expert e0+i first by i, inside a
 // segment by token. Up to 1024 tokens, one workgroup builds every table in
-// one launch (dispatch_small_kernel); above that, four kernels, no host
+// one launch (dispatch_small_kernel); above that, four kernels (three when the
+// rows are copied: placement then happens in the copy kernel), no host
 // synchronisation:
 //   1. histogram: one wave per chunk of 64 tokens counts its selections of
 //      every expert with LDS atomics -> chunk_table[e][chunk];
@@ -28,24 +29,37 @@
 
 namespace moe {
 
+// With mask_table, also stores for chunk c and local expert i the 64-bit set
+// of the chunk's lanes (tokens) that picked it, at mask_table[c E_local + i].
 __global__ void __launch_bounds__(kThreads)
 dispatch_hist_kernel(const int32_t* __restrict__ topk_idx, int T, int E, int k, int nchunks,
-                     int32_t* __restrict__ chunk_table) {
+                     int32_t* __restrict__ chunk_table, int e0, int E_local,
+                     unsigned long long* __restrict__ mask_table) {
   extern __shared__ int s_hist[];  // 4 waves x E
+  __shared__ unsigned long long s_mask[4][1024];
   const int w = threadIdx.x >> 6;
   const int lane = lane_id();
   int* hist = s_hist + w * E;
   for (int e = lane; e < E; e += 64) hist[e] = 0;
+  if (mask_table != nullptr)
+    for (int i = lane; i < E_local; i += 64) s_mask[w][i] = 0ull;
   __syncthreads();
   const int c = blockIdx.x * 4 + w;
   const int t = c * kChunk + lane;
   if (c < nchunks && t < T) {
     const int32_t* sel = topk_idx + int64_t(t) * k;
-    for (int j = 0; j < k; ++j) atomicAdd(&hist[sel[j]], 1);
+    for (int j = 0; j < k; ++j) {
+      const int e = sel[j];
+      atomicAdd(&hist[e], 1);
+      if (mask_table != nullptr && e >= e0 && e < e0 + E_local) atomicOr(&s_mask[w][e - e0], 1ull << lane);
+    }
   }
   __syncthreads();
-  if (c < nchunks)
+  if (c < nchunks) {
     for (int e = lane; e < E; e += 64) chunk_table[int64_t(e) * nchunks + c] = hist[e];
+    if (mask_table != nullptr)
+      for (int i = lane; i < E_local; i += 64) mask_table[int64_t(c) * E_local + i] = s_mask[w][i];
+  }
 }
 
 __global__ void __launch_bounds__(kThreads)
@@ -267,6 +281,93 @@ dispatch_copy_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__
   }
 }
 
+// Row placement fused into the row copy (moe_dispatch with T above the
+// one-workgroup size): one wave per token; the workgroup first scans the local
+// experts' counts into segment starts, then lane j of a token's wave places
+// slot j: row = segment start + the expert's selections in earlier chunks
+// (the scanned chunk table) + the chunk's earlier lanes that picked it (a
+// popcount of the stored lane set). Same rows as dispatch_index_kernel, one
+// launch fewer; then the token vector is copied to each of its rows.
+__global__ void __launch_bounds__(kThreads)
+dispatch_place_copy_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ topk_idx,
+                           const int32_t* __restrict__ chunk_base, const unsigned long long* __restrict__ mask_table,
+                           const int32_t* __restrict__ counts, int T, int H, int k, int e0, int E_local, int nchunks,
+                           int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src, int32_t* __restrict__ inv,
+                           uint16_t* __restrict__ x_perm) {
+  __shared__ int s_seg[1024 + 1];
+  __shared__ int s_tmp[4];
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = lane_id();
+  // this lane's slot and its placement inputs, loaded before the scan
+  int e = -1, base = 0;
+  unsigned long long m = 0ull;
+  if (t < T && lane < k) {
+    e = topk_idx[int64_t(t) * k + lane];
+    if (e >= e0 && e < e0 + E_local) {
+      const int c = t / kChunk;
+      base = chunk_base[int64_t(e) * nchunks + c];
+      m = mask_table[int64_t(c) * E_local + (e - e0)];
+    }
+  }
+  int cnt[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = threadIdx.x * 4 + q;
+    cnt[q] = i < E_local ? counts[e0 + i] : 0;
+  }
+  int tot;
+  int pre = block_exclusive_scan(cnt[0] + cnt[1] + cnt[2] + cnt[3], s_tmp, tot);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = threadIdx.x * 4 + q;
+    if (i < E_local) s_seg[i] = pre;
+    pre += cnt[q];
+  }
+  if (threadIdx.x == 0) s_seg[E_local] = tot;
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= E_local; i += kThreads) offsets[i] = s_seg[i];
+  if (t >= T) return;
+  int d = -1;
+  if (lane < k) {
+    if (e >= e0 && e < e0 + E_local) {
+      d = s_seg[e - e0] + base + __popcll(m & ((1ull << (t % kChunk)) - 1ull));
+      perm_src[d] = int32_t(int64_t(t) * k + lane);
+    }
+    inv[int64_t(t) * k + lane] = d;
+  }
+  const uint64_t dests = ballot(d >= 0);
+  if (dests == 0) return;
+  constexpr int U = 4;
+  const int nv = H / 8;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + int64_t(t) * H);
+  for (int v0 = 0; v0 < nv; v0 += 64 * U) {
+    u32x4 q[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = v0 + u * 64 + lane;
+      if (v < nv) q[u] = src[v];
+    }
+    uint64_t mm = dests;
+    while (mm) {
+      const int j = __ffsll((unsigned long long)mm) - 1;
+      mm &= mm - 1;
+      const int row = shfl(d, j);
+      u32x4* dst = reinterpret_cast<u32x4*>(x_perm + int64_t(row) * H);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * 64 + lane;
+        if (v < nv) __builtin_nontemporal_store(q[u], dst + v);
+      }
+    }
+  }
+}
+
+size_t dispatch_table_bytes(int T, int E) {
+  const size_t cells = size_t(E) * size_t(ceil_div(T, kChunk));
+  return ((cells + 1) / 2 * 2) * sizeof(int32_t) + cells * sizeof(unsigned long long);
+}
+
 hipError_t launch_dispatch_index(const int32_t* topk_idx, int T, int E, int k, int e0, int E_local, int32_t* counts,
                                  int32_t* offsets, int32_t* perm_src, int32_t* inv, int32_t* chunk_table,
                                  hipStream_t stream) {
@@ -292,7 +393,7 @@ hipError_t launch_dispatch_index(const int32_t* topk_idx, int T, int E, int k, i
   const int nchunks = int(ceil_div(T, kChunk));
   const unsigned wgs = unsigned(ceil_div(nchunks, 4));
   hipLaunchKernelGGL(dispatch_hist_kernel, dim3(wgs), dim3(kThreads), size_t(4) * E * sizeof(int), stream,
-                     topk_idx, T, E, k, nchunks, chunk_table);
+                     topk_idx, T, E, k, nchunks, chunk_table, e0, E_local, nullptr);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(unsigned(E)), dim3(kThreads), 0, stream, chunk_table, nchunks,
@@ -320,11 +421,28 @@ hipError_t launch_dispatch_index(const int32_t* topk_idx, int T, int E, int k, i
 hipError_t launch_dispatch(const uint16_t* x, const int32_t* topk_idx, int T, int H, int E, int k, int e0,
                            int E_local, int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* inv,
                            uint16_t* x_perm, int32_t* chunk_table, hipStream_t stream) {
-  hipError_t err =
-      launch_dispatch_index(topk_idx, T, E, k, e0, E_local, counts, offsets, perm_src, inv, chunk_table, stream);
+  if (T <= kSmallTokens) {
+    hipError_t err =
+        launch_dispatch_index(topk_idx, T, E, k, e0, E_local, counts, offsets, perm_src, inv, chunk_table, stream);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(dispatch_copy_kernel, dim3(unsigned(ceil_div(T, 4))), dim3(kThreads), 0, stream, x, inv, T,
+                       H, k, x_perm);
+    return hipGetLastError();
+  }
+  const int nchunks = int(ceil_div(T, kChunk));
+  const size_t cells = size_t(E) * size_t(nchunks);
+  auto* masks = reinterpret_cast<unsigned long long*>(chunk_table + (cells + 1) / 2 * 2);
+  const unsigned wgs = unsigned(ceil_div(nchunks, 4));
+  hipLaunchKernelGGL(dispatch_hist_kernel, dim3(wgs), dim3(kThreads), size_t(4) * E * sizeof(int), stream,
+                     topk_idx, T, E, k, nchunks, chunk_table, e0, E_local, masks);
+  hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(dispatch_copy_kernel, dim3(unsigned(ceil_div(T, 4))), dim3(kThreads), 0, stream, x, inv, T,
-                     H, k, x_perm);
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(unsigned(E)), dim3(kThreads), 0, stream, chunk_table, nchunks,
+                     counts);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(dispatch_place_copy_kernel, dim3(unsigned(ceil_div(T, 4))), dim3(kThreads), 0, stream, x,
+                     topk_idx, chunk_table, masks, counts, T, H, k, e0, E_local, nchunks, offsets, perm_src, inv,
+                     x_perm);
   return hipGetLastError();
 }
 

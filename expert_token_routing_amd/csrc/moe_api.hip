@@ -58,7 +58,6 @@ struct ForwardLayout {
 static ForwardLayout forward_layout(int T, int H, int I, int E, int k, int E_local) {
   ForwardLayout L{};
   const int64_t cap = min_capacity(T, k, E_local);
-  const int64_t nchunks = ceil_div(T, kChunk);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -74,7 +73,7 @@ static ForwardLayout forward_layout(int T, int H, int I, int E, int k, int E_loc
   L.offsets = take(size_t(E_local + 1) * sizeof(int32_t));
   L.perm_src = take(size_t(cap) * sizeof(int32_t));
   L.inv = take(size_t(T) * k * sizeof(int32_t));
-  L.chunks = take(size_t(E) * nchunks * sizeof(int32_t));
+  L.chunks = take(dispatch_table_bytes(T, E));
   L.x_perm = take(size_t(cap) * H * sizeof(uint16_t));
   L.h = take(size_t(cap) * I * sizeof(uint16_t));
   L.out = take(size_t(cap) * H * sizeof(uint16_t));
@@ -127,7 +126,7 @@ int moe_route(const moe_bf16* x, const float* w_router, const float* bias, int T
 size_t moe_dispatch_workspace_size(int T, int E, int k) {
   (void)k;
   if (T < 0 || E <= 0) return 0;
-  return align_up(size_t(E) * size_t(ceil_div(T, kChunk)) * sizeof(int32_t));
+  return align_up(dispatch_table_bytes(T, E));
 }
 
 int moe_dispatch(const moe_bf16* x, const int32_t* topk_idx, int T, int H, int E, int k, int e0, int E_local,

@@ -47,6 +47,11 @@ hipError_t launch_expert_gemm1_gather(const uint16_t* x, const int32_t* perm_src
                                       const uint16_t* w_gate_up, int H, int I, int E_local, int64_t capacity,
                                       uint16_t* h, hipStream_t stream);
 
+// Bytes of the dispatch tables in the workspace: the per-chunk histogram
+// table [E][ceil(T/64)] i32, then the per-chunk lane sets (at most E per
+// chunk) u64.
+size_t dispatch_table_bytes(int T, int E);
+
 // Dispatch without the row copy (counts, offsets, perm_src, inv only).
 hipError_t launch_dispatch_index(const int32_t* topk_idx, int T, int E, int k, int e0, int E_local, int32_t* counts,
                                  int32_t* offsets, int32_t* perm_src, int32_t* inv, int32_t* chunk_table,

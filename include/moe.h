@@ -101,7 +101,9 @@ int moe_route(const moe_bf16* x, const float* w_router, const float* bias, int T
 /* Dispatch: group the local (token, slot) selections by expert.             */
 /* ------------------------------------------------------------------------ */
 
-/* Bytes of device workspace moe_dispatch needs (per-chunk histograms). */
+/* Bytes of device workspace moe_dispatch needs (per-64-token-chunk histograms
+ * of all E experts and per-chunk 64-bit sets of the tokens that picked each
+ * local expert). */
 size_t moe_dispatch_workspace_size(int T, int E, int k);
 
 /*
