@@ -28,6 +28,11 @@
 namespace moe {
 
 constexpr int kMaxLocal = 1024;
+// Row caps the panel GEMM chooses from per launch (largest first; all are
+// multiples of 32 and at most the 288 rows a tile holds).
+constexpr int kRowCaps = 6;
+__device__ constexpr int kRowCap[kRowCaps] = {288, 256, 224, 192, 160, 128};
+constexpr int kRowCapMin = 128;
 
 template <int BM, bool SWIGLU>
 __global__ void __launch_bounds__(kThreads)
@@ -370,23 +375,63 @@ panel_gemm_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __rest
   __shared__ int s_off[kMaxLocal + 1];
   __shared__ int s_tpre[kMaxLocal + 1];
   __shared__ int s_tmp[dma::kWaves];
+  __shared__ int s_cand[2 * kRowCaps];
   MOE_LDS char* lds = (MOE_LDS char*)smem;
 
   const int ntn = SWIGLU ? (N + kBN / 2 - 1) / (kBN / 2) : (N + kBN - 1) / kBN;
   constexpr int kPerT = (kMaxLocal + dma::kThreads - 1) / dma::kThreads;
-  int mt[kPerT];
-  int sum = 0;
+  int me[kPerT];
+  if (threadIdx.x < 2 * kRowCaps) s_cand[threadIdx.x] = 0;
 #pragma unroll
   for (int q = 0; q < kPerT; ++q) {
     const int i = threadIdx.x * kPerT + q;
-    mt[q] = 0;
+    me[q] = 0;
     if (i < E_local) {
       const int64_t a = min<int64_t>(max<int64_t>(offsets[i], 0), capacity);
       const int64_t b = max<int64_t>(a, min<int64_t>(offsets[i + 1], capacity));
       s_off[i] = int(a);
-      mt[q] = int((b - a + kRowsMax - 1) / kRowsMax) * ntn;
+      me[q] = int(b - a);
       if (i == E_local - 1) s_off[E_local] = int(b);
     }
+  }
+  __syncthreads();
+  // Row cap of the launch: for each candidate cap, the tile count and the
+  // tallest row block; the cap whose estimate ceil(tiles / grid) x (tallest
+  // block + 256) is lowest wins (a tile's time grows with its rows plus its
+  // 256 weight columns), the larger cap on ties. Every workgroup gets the same
+  // sums and picks the same cap.
+#pragma unroll
+  for (int c = 0; c < kRowCaps; ++c) {
+    int tl = 0, hm = 0;
+#pragma unroll
+    for (int q = 0; q < kPerT; ++q) {
+      if (me[q] > 0) {
+        const int nrt = (me[q] + kRowCap[c] - 1) / kRowCap[c];
+        tl += nrt * ntn;
+        hm = max(hm, (((me[q] + nrt - 1) / nrt) + 15) & ~15);
+      }
+    }
+    if (tl > 0) atomicAdd(&s_cand[c], tl);
+    if (hm > 0) atomicMax(&s_cand[kRowCaps + c], hm);
+  }
+  __syncthreads();
+  int row_cap = kRowCap[0];
+  {
+    int64_t best = -1;
+#pragma unroll
+    for (int c = 0; c < kRowCaps; ++c) {
+      const int64_t est = int64_t((s_cand[c] + int(gridDim.x) - 1) / int(gridDim.x)) * (s_cand[kRowCaps + c] + kBN);
+      if (best < 0 || est < best) {
+        best = est;
+        row_cap = kRowCap[c];
+      }
+    }
+  }
+  int mt[kPerT];
+  int sum = 0;
+#pragma unroll
+  for (int q = 0; q < kPerT; ++q) {
+    mt[q] = (me[q] + row_cap - 1) / row_cap * ntn;
     sum += mt[q];
   }
   int total;
@@ -418,7 +463,7 @@ panel_gemm_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __rest
     const int t0 = __builtin_amdgcn_readfirstlane(s_tpre[e]);
     const int seg0 = __builtin_amdgcn_readfirstlane(s_off[e]);
     const int m_e = __builtin_amdgcn_readfirstlane(s_off[e + 1]) - seg0;
-    const int nrt = (m_e + kRowsMax - 1) / kRowsMax;
+    const int nrt = (m_e + row_cap - 1) / row_cap;
     const int local = tile - t0;
     const int nj = local / nrt;
     const int mi = local - nj * nrt;
@@ -482,7 +527,7 @@ unsigned dma_grid(int64_t tiles) {
 hipError_t launch_expert_gemm1(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_gate_up, int H,
                                int I, int E_local, int64_t capacity, uint16_t* h, hipStream_t stream) {
   if (H % dma::kBK == 0) {
-    const int64_t tiles = (ceil_div(capacity, dma::panel::kRowsMax) + E_local) * ceil_div(I, dma::panel::kBN / 2);
+    const int64_t tiles = (ceil_div(capacity, kRowCapMin) + E_local) * ceil_div(I, dma::panel::kBN / 2);
     hipLaunchKernelGGL((panel_gemm_kernel<true>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream, x_perm, H,
                        offsets, E_local, capacity, w_gate_up, int64_t(H) * 2 * I, 2 * I, h, I, H, I, I, nullptr, 1, 0);
     return hipGetLastError();
@@ -497,7 +542,7 @@ hipError_t launch_expert_gemm1(const uint16_t* x_perm, const int32_t* offsets, c
 hipError_t launch_expert_gemm2(const uint16_t* h, const int32_t* offsets, const uint16_t* w_down, int H, int I,
                                int E_local, int64_t capacity, uint16_t* out, hipStream_t stream) {
   if (I % dma::kBK == 0) {
-    const int64_t tiles = (ceil_div(capacity, dma::panel::kRowsMax) + E_local) * ceil_div(H, dma::panel::kBN);
+    const int64_t tiles = (ceil_div(capacity, kRowCapMin) + E_local) * ceil_div(H, dma::panel::kBN);
     hipLaunchKernelGGL((panel_gemm_kernel<false>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream, h, I,
                        offsets, E_local, capacity, w_down, int64_t(I) * H, H, out, H, I, H, 0, nullptr, 1, 0);
     return hipGetLastError();
@@ -514,7 +559,7 @@ bool expert_gemm1_can_gather(int T, int H) { return H % dma::kBK == 0 && int64_t
 hipError_t launch_expert_gemm1_gather(const uint16_t* x, const int32_t* perm_src, int T, int k, const int32_t* offsets,
                                       const uint16_t* w_gate_up, int H, int I, int E_local, int64_t capacity,
                                       uint16_t* h, hipStream_t stream) {
-  const int64_t tiles = (ceil_div(capacity, dma::panel::kRowsMax) + E_local) * ceil_div(I, dma::panel::kBN / 2);
+  const int64_t tiles = (ceil_div(capacity, kRowCapMin) + E_local) * ceil_div(I, dma::panel::kBN / 2);
   hipLaunchKernelGGL((panel_gemm_kernel<true>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream, x, H, offsets,
                      E_local, capacity, w_gate_up, int64_t(H) * 2 * I, 2 * I, h, I, H, I, I, perm_src, k, T);
   return hipGetLastError();
