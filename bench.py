@@ -379,12 +379,30 @@ def main():
                 "stage_ms": {n: round(float(v), 4) for n, v in zip(STAGES, cms.mean(0))}}
         del scratch
 
+    # moe_forward_fused: the combine of single-selection tokens in the down
+    # GEMM's epilogue, timed the same way right after (same inputs, same y)
+    fev = new_events(args.steps)
+    for _ in range(max(2, args.warmup // 4)):
+        M.moe_forward_profiled(x, wr, bias, gu, dn, cfg.k, cfg.e0, cfg.renormalize, y, ws, wev[0], stream=stream,
+                               fused=True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        M.moe_forward_profiled(x, wr, bias, gu, dn, cfg.k, cfg.e0, cfg.renormalize, y, ws, fev[i], stream=stream,
+                               fused=True)
+    torch.cuda.synchronize()
+    fused_wall = time.perf_counter() - t1
+    fused_stage = np.array([[fev[i][j].elapsed_time(fev[i][j + 1]) for j in range(5)]
+                            for i in range(args.steps)]).mean(0)
+    log("[bench] fused-combine stage ms: " + ", ".join(f"{n}={v:.3f}" for n, v in zip(STAGES, fused_stage)))
+
     # realised routing of the timed steps (identical every step)
     lay = M.forward_workspace_layout(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, cfg.E_local)
     offs = ws[lay["offsets"]:lay["offsets"] + 4 * (cfg.E_local + 1)].view(torch.int32).cpu().numpy()
     inv = ws[lay["inv"]:lay["inv"] + 4 * cfg.T * cfg.k].view(torch.int32).reshape(cfg.T, cfg.k).cpu().numpy()
     N = int(offs[-1])
     U = int((inv >= 0).any(1).sum())
+    single = int(((inv >= 0).sum(1) == 1).sum())
     fused = cfg.H % 32 == 0 and cfg.T * cfg.H * 2 < 2 ** 31
     E_hit = int((np.diff(offs) > 0).sum())
     work = algorithmic(cfg, N, U, E_hit, fused)
@@ -500,6 +518,14 @@ def main():
         "stages": stages,
         "dispatch_rows": dispatch_rows,
         "combine_f32": combine_f32,
+        "fused_combine": {
+            "value": round(cfg.T * args.steps / fused_wall, 1), "unit": "tokens/s",
+            "ms_per_step": round(fused_wall / args.steps * 1e3, 4),
+            "stage_us": {n: round(float(v) * 1e3, 2) for n, v in zip(STAGES, fused_stage)},
+            "tokens_single_local_pick": single,
+            "note": "moe_forward_fused: tokens with exactly one local selection are weighted and written to y by "
+                    "the down GEMM's epilogue, the combine kernel sums the rest; y is bit-identical to "
+                    "moe_forward's"},
         "layer_tflops": round(total_flop / (ms_per_step * 1e-3) / 1e12, 2),
         "realised": {"N_local_rows": N, "U_tokens_with_local_pick": U,
                      "rows_per_local_expert_max": int(np.diff(offs).max()),

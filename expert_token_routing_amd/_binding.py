@@ -38,6 +38,10 @@ SIGNATURES = {
                                 _P, _P, c_size_t, _P]),
     "moe_forward_profiled": (c_int, [_P, _P, _P, _P, _P, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                      _P, _P, c_size_t, _P, _P]),
+    "moe_forward_fused": (c_int, [_P, _P, _P, _P, _P, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                  _P, _P, c_size_t, _P]),
+    "moe_forward_fused_profiled": (c_int, [_P, _P, _P, _P, _P, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                           c_int, _P, _P, c_size_t, _P, _P]),
 }
 
 _lib = None
@@ -260,16 +264,26 @@ def moe_forward_f32(x, w_router, bias, w_gate_up, w_down, k, e0, renormalize=Tru
                     y, workspace, stream)
 
 
+def moe_forward_fused(x, w_router, bias, w_gate_up, w_down, k, e0, renormalize=True, *, y=None, workspace=None,
+                      stream=None):
+    """moe_forward with the combine of tokens that have exactly one local
+    selection done in the down GEMM's epilogue; y equals moe_forward's."""
+    return _forward("moe_forward_fused", _torch().bfloat16, x, w_router, bias, w_gate_up, w_down, k, e0,
+                    renormalize, y, workspace, stream)
+
+
 def moe_forward_profiled(x, w_router, bias, w_gate_up, w_down, k, e0, renormalize, y, workspace, events,
-                         stream=None):
-    """moe_forward into preallocated ``y`` / ``workspace``, recording the six
-    torch.cuda.Event objects in ``events`` (already recorded once, so they
-    exist) around the router, dispatch, gate/up GEMM, down GEMM and combine."""
+                         stream=None, fused=False):
+    """moe_forward (moe_forward_fused with ``fused``) into preallocated ``y`` /
+    ``workspace``, recording the six torch.cuda.Event objects in ``events``
+    (already recorded once, so they exist) around the router, dispatch,
+    gate/up GEMM, down GEMM and combine."""
     T, H = x.shape
     E = w_router.shape[0]
     E_local, _, I2 = w_gate_up.shape
     arr = (c_void_p * 6)(*[c_void_p(ev.cuda_event) for ev in events])
-    st = lib().moe_forward_profiled(_ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate_up), _ptr(w_down), T, H,
-                                    I2 // 2, E, k, e0, E_local, int(bool(renormalize)), _ptr(y), _ptr(workspace),
-                                    workspace.numel(), arr, _stream(stream, x.device))
-    check(st, "moe_forward_profiled")
+    name = "moe_forward_fused_profiled" if fused else "moe_forward_profiled"
+    st = getattr(lib(), name)(_ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate_up), _ptr(w_down), T, H, I2 // 2, E,
+                              k, e0, E_local, int(bool(renormalize)), _ptr(y), _ptr(workspace), workspace.numel(),
+                              arr, _stream(stream, x.device))
+    check(st, name)

@@ -20,7 +20,7 @@
 
 namespace moe {
 
-template <int KMAX, bool F32>
+template <int KMAX, bool F32, bool SKIP1>
 __global__ void __launch_bounds__(kThreads)
 combine_kernel(const uint16_t* __restrict__ expert_out, const int32_t* __restrict__ inv,
                const float* __restrict__ topk_w, int T, int H, int k, int vpb, void* __restrict__ y) {
@@ -49,6 +49,9 @@ combine_kernel(const uint16_t* __restrict__ expert_out, const int32_t* __restric
       }
     }
   }
+  // With SKIP1 the down GEMM's epilogue already wrote tokens with exactly
+  // one local slot.
+  if (SKIP1 && nl == 1) return;
   // Start from -0 so that a single term passes through bit for bit (-0 + -0 = -0);
   // a token with no local slot is written as +0.
   const float init = nl > 0 ? -0.f : 0.f;
@@ -126,7 +129,7 @@ combine_kernel(const uint16_t* __restrict__ expert_out, const int32_t* __restric
   }
 }
 
-template <bool F32>
+template <bool F32, bool SKIP1>
 static void launch_combine_t(const uint16_t* expert_out, const int32_t* inv, const float* topk_w, int T, int H,
                              int k, void* y, hipStream_t stream) {
   // Few tokens: each token's row is cut into column blocks (blockIdx.y) of
@@ -137,7 +140,7 @@ static void launch_combine_t(const uint16_t* expert_out, const int32_t* inv, con
   const int vpb = int(ceil_div(ceil_div(nv, want), 64) * 64);
   const dim3 grid(unsigned(ceil_div(T, 4)), unsigned(ceil_div(nv, vpb)));
 #define MOE_COMBINE_LAUNCH(KM)                                                                                     \
-  hipLaunchKernelGGL((combine_kernel<KM, F32>), grid, dim3(kThreads), 0, stream, expert_out, inv, topk_w, T, H, k, \
+  hipLaunchKernelGGL((combine_kernel<KM, F32, SKIP1>), grid, dim3(kThreads), 0, stream, expert_out, inv, topk_w, T, H, k, \
                      vpb, y)
   if (k <= 1)
     MOE_COMBINE_LAUNCH(1);
@@ -155,11 +158,43 @@ static void launch_combine_t(const uint16_t* expert_out, const int32_t* inv, con
 }
 
 hipError_t launch_combine(const uint16_t* expert_out, const int32_t* inv, const float* topk_w, int T, int H, int k,
-                          void* y, bool y_f32, hipStream_t stream) {
+                          void* y, bool y_f32, hipStream_t stream, bool skip_single) {
   if (y_f32)
-    launch_combine_t<true>(expert_out, inv, topk_w, T, H, k, y, stream);
+    launch_combine_t<true, false>(expert_out, inv, topk_w, T, H, k, y, stream);
+  else if (skip_single)
+    launch_combine_t<false, true>(expert_out, inv, topk_w, T, H, k, y, stream);
   else
-    launch_combine_t<false>(expert_out, inv, topk_w, T, H, k, y, stream);
+    launch_combine_t<false, false>(expert_out, inv, topk_w, T, H, k, y, stream);
+  return hipGetLastError();
+}
+
+// For the combine fused into the down GEMM: one thread per token counts its
+// local slots; the row of a token with exactly one gets {token, weight bits},
+// every other local row {-1, 0}. Every local row is written once.
+__global__ void __launch_bounds__(kThreads)
+single_rows_kernel(const int32_t* __restrict__ inv, const float* __restrict__ topk_w, int T, int k,
+                   int2* __restrict__ row_info) {
+  const int t = blockIdx.x * kThreads + threadIdx.x;
+  if (t >= T) return;
+  const int32_t* d = inv + int64_t(t) * k;
+  int nl = 0, js = 0;
+  for (int j = 0; j < k; ++j)
+    if (d[j] >= 0) {
+      ++nl;
+      js = j;
+    }
+  if (nl == 1) {
+    row_info[d[js]] = make_int2(t, __float_as_int(topk_w[int64_t(t) * k + js]));
+  } else {
+    for (int j = 0; j < k; ++j)
+      if (d[j] >= 0) row_info[d[j]] = make_int2(-1, 0);
+  }
+}
+
+hipError_t launch_single_rows(const int32_t* inv, const float* topk_w, int T, int k, int2* row_info,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(single_rows_kernel, dim3(unsigned(ceil_div(T, kThreads))), dim3(kThreads), 0, stream, inv,
+                     topk_w, T, k, row_info);
   return hipGetLastError();
 }
 

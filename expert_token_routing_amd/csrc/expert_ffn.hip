@@ -193,11 +193,15 @@ __device__ __forceinline__ void alternate_mfma_reads() {
 
 // One tile: FMT fragments per wave row (16 * kWR * FMT >= rows), `rows` rows
 // from the row source, weight columns given by col_of.
-template <int FMT, bool SWIGLU, typename SrcRow, typename ColOf>
+// FUSE (down GEMM only): s_ri holds, for each tile row, the destination
+// token and combine weight of a row whose token has exactly one local
+// selection (token -1 otherwise); such rows go to y as the combine would
+// write them, the others to C.
+template <int FMT, bool SWIGLU, bool FUSE, typename SrcRow, typename ColOf>
 __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __restrict__ Abase, int64_t a_bytes,
                                          int lda, int rows, SrcRow src_row, const uint16_t* __restrict__ We, int ldw,
                                          int K, ColOf col_of, int out_c0, int N, uint16_t* __restrict__ C, int ldc,
-                                         int r0) {
+                                         int r0, const MOE_LDS int* s_ri, uint16_t* __restrict__ y) {
   const int w = threadIdx.x >> 6, wm = w % kWR, wn = w / kWR;
   const int lane = lane_id();
   // GEMM1 multiplies weight x row fragments, i.e. produces the transposed
@@ -340,6 +344,33 @@ __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __re
         }
       }
     }
+  } else if constexpr (FUSE) {
+    // as below; a row of a single-selection token becomes w * out in its
+    // token's y row, rounded like the combine's one-term sum (fmaf onto -0,
+    // then bf16). The row info is read at constant offsets from one base
+    // (immediate LDS offsets, no per-row address registers).
+    typedef int i32x2v __attribute__((ext_vector_type(2)));
+    const MOE_LDS i32x2v* const rib = reinterpret_cast<const MOE_LDS i32x2v*>(s_ri) + 16 * wm + g4;
+#pragma unroll
+    for (int i = 0; i < FMT; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = 16 * (kWR * i + wm) + g4 + v;
+        if (row < rows) {
+          const i32x2v ri = rib[16 * kWR * i + v];
+          const int dst = ri.x;
+          const float wt = __int_as_float(ri.y);
+          uint16_t* const base = dst >= 0 ? y + int64_t(dst) * ldc : C + int64_t(r0 + row) * ldc;
+#pragma unroll
+          for (int j = 0; j < kFN; ++j) {
+            const int col = out_c0 + 64 * wn + 16 * j + l16;
+            if (col < N) {
+              const uint32_t ob = f32_to_bf16_bits(acc[i][j][v]);
+              base[col] = uint16_t(dst >= 0 ? f32_to_bf16_bits(fmaf(wt, bf16_to_f32(uint16_t(ob)), -0.f)) : ob);
+            }
+          }
+        }
+      }
   } else {
     // fragment (i, j), lane l, element v is tile row 16 (kWR i + wm) + 4 (l >> 4) + v,
     // tile column 64 wn + 16 j + (l & 15)
@@ -364,14 +395,23 @@ __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __re
 // inside the expert (the row blocks sharing a weight panel are adjacent and
 // run together); each XCD takes a contiguous range, dealt round robin to its
 // workgroups (workgroup b runs on XCD b % 8).
-template <bool SWIGLU>
+// FUSE (down GEMM): row_info[n] = {token, combine weight bits} for row n of a
+// token with exactly one local selection, {-1, 0} otherwise; those rows are
+// written to y [T, ldc] instead of C.
+template <bool SWIGLU, bool FUSE = false>
 __global__ void __launch_bounds__(dma::kThreads)
 panel_gemm_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __restrict__ offsets, int E_local,
                   int64_t capacity, const uint16_t* __restrict__ W, int64_t w_expert_stride, int ldw,
                   uint16_t* __restrict__ C, int ldc, int K, int N, int up_off, const int32_t* __restrict__ gather_src,
-                  int gather_k, int gather_rows) {
+                  int gather_k, int gather_rows, const int2* __restrict__ row_info, uint16_t* __restrict__ y) {
   using namespace dma::panel;
+  static_assert(!(FUSE && SWIGLU), "the combine is fused into the down GEMM only");
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  // row info of the tile: 3 waves x 64 lanes x 16 bytes cover the 288 rows.
+  // Two buffers by tile parity: a wave copies the next tile's info while
+  // slower waves may still read this tile's in their epilogue (the next
+  // tile's first barrier orders everything after that).
+  __shared__ __attribute__((aligned(1024))) int s_ri[FUSE ? 2 * 768 : 4];
   __shared__ int s_off[kMaxLocal + 1];
   __shared__ int s_tpre[kMaxLocal + 1];
   __shared__ int s_tmp[dma::kWaves];
@@ -450,6 +490,7 @@ panel_gemm_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __rest
   const int per_xcd = gridDim.x / nxcd;
   const int lo_t = int((int64_t(total) * xcd) / nxcd);
   const int hi_t = int((int64_t(total) * (xcd + 1)) / nxcd);
+  int parity = 0;
   for (int tile = lo_t + int(blockIdx.x / nxcd); tile < hi_t; tile += per_xcd) {
     int lo = 0, hi = E_local - 1;
     while (lo < hi) {
@@ -472,6 +513,8 @@ panel_gemm_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __rest
     const int rows = min(height, seg0 + m_e - r0);
     if (rows <= 0) continue;
     const uint16_t* We = W + int64_t(e) * w_expert_stride;
+    MOE_LDS int* const ri_buf = (MOE_LDS int*)s_ri + (FUSE ? 768 * parity : 0);
+    parity ^= 1;
     auto col_of = [&](int s0) -> int {
       if (SWIGLU) {  // tile column s: wave column s/64, gate (s%64 < 32) or up of output o0 + 32*(s/64) + s%32
         const int q = s0 & 63;
@@ -485,15 +528,28 @@ panel_gemm_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __rest
     };
     const int out_c0 = SWIGLU ? nj * (kBN / 2) : nj * kBN;
     const int fmt = (rows + 16 * kWR - 1) / (16 * kWR);
+    if constexpr (FUSE) {
+      // direct-to-LDS copy of the tile rows' info (bytes beyond the tile's
+      // rows read as zero); issued before the tile's first stage, so the
+      // tile's first stage wait covers it
+      const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      if (w < 3) {
+        const dma::i32x4 rs = dma::buffer_rsrc(row_info + r0, int64_t(rows) * 8);
+        // the wave's offset goes in the per-lane offset, which the buffer's
+        // range check covers (the scalar offset is not checked)
+        dma::dma16(rs, 1024u * uint32_t(w) + 16u * uint32_t(lane_id()), 0u, (MOE_LDS char*)ri_buf + 1024 * w);
+      }
+    }
     auto go = [&](auto fm_t) {
       constexpr int FMT = decltype(fm_t)::value;
       if (gather_src != nullptr) {
-        panelffn::run_tile<FMT, SWIGLU>(lds, A, int64_t(gather_rows) * lda * 2, lda, rows,
-                                        [&](int r) { return gather_src[r0 + r] / gather_k; }, We, ldw, K, col_of,
-                                        out_c0, N, C, ldc, r0);
+        panelffn::run_tile<FMT, SWIGLU, FUSE>(lds, A, int64_t(gather_rows) * lda * 2, lda, rows,
+                                              [&](int r) { return gather_src[r0 + r] / gather_k; }, We, ldw, K,
+                                              col_of, out_c0, N, C, ldc, r0, (const MOE_LDS int*)ri_buf, y);
       } else {
-        panelffn::run_tile<FMT, SWIGLU>(lds, A + int64_t(r0) * lda, int64_t(rows) * lda * 2, lda, rows,
-                                        [](int r) { return r; }, We, ldw, K, col_of, out_c0, N, C, ldc, r0);
+        panelffn::run_tile<FMT, SWIGLU, FUSE>(lds, A + int64_t(r0) * lda, int64_t(rows) * lda * 2, lda, rows,
+                                              [](int r) { return r; }, We, ldw, K, col_of, out_c0, N, C, ldc, r0,
+                                              (const MOE_LDS int*)ri_buf, y);
       }
     };
     switch (fmt) {
@@ -529,7 +585,7 @@ hipError_t launch_expert_gemm1(const uint16_t* x_perm, const int32_t* offsets, c
   if (H % dma::kBK == 0) {
     const int64_t tiles = (ceil_div(capacity, kRowCapMin) + E_local) * ceil_div(I, dma::panel::kBN / 2);
     hipLaunchKernelGGL((panel_gemm_kernel<true>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream, x_perm, H,
-                       offsets, E_local, capacity, w_gate_up, int64_t(H) * 2 * I, 2 * I, h, I, H, I, I, nullptr, 1, 0);
+                       offsets, E_local, capacity, w_gate_up, int64_t(H) * 2 * I, 2 * I, h, I, H, I, I, nullptr, 1, 0, nullptr, nullptr);
     return hipGetLastError();
   }
   const int64_t mt_bound = ceil_div(capacity, kFfnBM) + E_local;
@@ -544,13 +600,25 @@ hipError_t launch_expert_gemm2(const uint16_t* h, const int32_t* offsets, const 
   if (I % dma::kBK == 0) {
     const int64_t tiles = (ceil_div(capacity, kRowCapMin) + E_local) * ceil_div(H, dma::panel::kBN);
     hipLaunchKernelGGL((panel_gemm_kernel<false>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream, h, I,
-                       offsets, E_local, capacity, w_down, int64_t(I) * H, H, out, H, I, H, 0, nullptr, 1, 0);
+                       offsets, E_local, capacity, w_down, int64_t(I) * H, H, out, H, I, H, 0, nullptr, 1, 0, nullptr, nullptr);
     return hipGetLastError();
   }
   const int64_t mt_bound = ceil_div(capacity, kFfnBM) + E_local;
   const unsigned grid = persistent_grid(mt_bound * ceil_div(H, 256));
   hipLaunchKernelGGL((grouped_gemm_kernel<kFfnBM, false>), dim3(grid), dim3(kThreads), 0, stream, h, I, offsets,
                      E_local, capacity, w_down, int64_t(I) * H, H, out, H, I, H, 0);
+  return hipGetLastError();
+}
+
+bool expert_gemm2_can_fuse(int I) { return I % dma::kBK == 0; }
+
+hipError_t launch_expert_gemm2_fused(const uint16_t* h, const int32_t* offsets, const uint16_t* w_down, int H, int I,
+                                     int E_local, int64_t capacity, const int2* row_info, uint16_t* out, uint16_t* y,
+                                     hipStream_t stream) {
+  const int64_t tiles = (ceil_div(capacity, kRowCapMin) + E_local) * ceil_div(H, dma::panel::kBN);
+  hipLaunchKernelGGL((panel_gemm_kernel<false, true>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream, h, I,
+                     offsets, E_local, capacity, w_down, int64_t(I) * H, H, out, H, I, H, 0, nullptr, 1, 0, row_info,
+                     y);
   return hipGetLastError();
 }
 
@@ -561,7 +629,8 @@ hipError_t launch_expert_gemm1_gather(const uint16_t* x, const int32_t* perm_src
                                       uint16_t* h, hipStream_t stream) {
   const int64_t tiles = (ceil_div(capacity, kRowCapMin) + E_local) * ceil_div(I, dma::panel::kBN / 2);
   hipLaunchKernelGGL((panel_gemm_kernel<true>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream, x, H, offsets,
-                     E_local, capacity, w_gate_up, int64_t(H) * 2 * I, 2 * I, h, I, H, I, I, perm_src, k, T);
+                     E_local, capacity, w_gate_up, int64_t(H) * 2 * I, 2 * I, h, I, H, I, I, perm_src, k, T, nullptr,
+                     nullptr);
   return hipGetLastError();
 }
 

@@ -53,7 +53,8 @@ static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 // Workspace layout of moe_forward.
 struct ForwardLayout {
-  size_t planes, part, logits, topk_idx, topk_w, counts, offsets, perm_src, inv, chunks, x_perm, h, out, total;
+  size_t planes, part, logits, topk_idx, topk_w, counts, offsets, perm_src, inv, chunks, x_perm, h, out, row_info,
+      total;
 };
 static ForwardLayout forward_layout(int T, int H, int I, int E, int k, int E_local) {
   ForwardLayout L{};
@@ -77,6 +78,7 @@ static ForwardLayout forward_layout(int T, int H, int I, int E, int k, int E_loc
   L.x_perm = take(size_t(cap) * H * sizeof(uint16_t));
   L.h = take(size_t(cap) * I * sizeof(uint16_t));
   L.out = take(size_t(cap) * H * sizeof(uint16_t));
+  L.row_info = take(size_t(cap) * sizeof(int2));
   L.total = o;
   return L;
 }
@@ -195,7 +197,7 @@ int moe_forward_workspace_layout(int T, int H, int I, int E, int k, int E_local,
 static int forward_impl(const moe_bf16* x, const float* w_router, const float* bias, const moe_bf16* w_gate_up,
                         const moe_bf16* w_down, int T, int H, int I, int E, int k, int e0, int E_local,
                         int renormalize, void* y, bool y_f32, void* workspace, size_t workspace_bytes,
-                        hipEvent_t* events, hipStream_t stream) {
+                        hipEvent_t* events, hipStream_t stream, bool fuse_combine = false) {
   int st = check_route_dims(T, H, E, k);
   if (st != MOE_OK) return st;
   if ((st = check_local(E, e0, E_local)) != MOE_OK) return st;
@@ -222,6 +224,9 @@ static int forward_impl(const moe_bf16* x, const float* w_router, const float* b
   uint16_t* x_perm = static_cast<uint16_t*>(at(L.x_perm));
   uint16_t* h = static_cast<uint16_t*>(at(L.h));
   uint16_t* out = static_cast<uint16_t*>(at(L.out));
+  int2* row_info = static_cast<int2*>(at(L.row_info));
+  // the combine of single-selection tokens runs in the down GEMM's epilogue
+  const bool fuse = fuse_combine && !y_f32 && expert_gemm2_can_fuse(I);
   auto mark = [&](int i) { return events ? hipEventRecord(events[i], stream) : hipSuccess; };
 
   hipError_t err = mark(0);
@@ -236,14 +241,18 @@ static int forward_impl(const moe_bf16* x, const float* w_router, const float* b
     err = gather ? launch_dispatch_index(topk_idx, T, E, k, e0, E_local, counts, offsets, perm_src, inv, chunks, stream)
                  : launch_dispatch(x, topk_idx, T, H, E, k, e0, E_local, counts, offsets, perm_src, inv, x_perm,
                                    chunks, stream);
+  if (err == hipSuccess && fuse) err = launch_single_rows(inv, topk_w, T, k, row_info, stream);
   if (err == hipSuccess) err = mark(2);
   if (err == hipSuccess)
     err = gather ? launch_expert_gemm1_gather(x, perm_src, T, k, offsets, w_gate_up, H, I, E_local, cap, h, stream)
                  : launch_expert_gemm1(x_perm, offsets, w_gate_up, H, I, E_local, cap, h, stream);
   if (err == hipSuccess) err = mark(3);
-  if (err == hipSuccess) err = launch_expert_gemm2(h, offsets, w_down, H, I, E_local, cap, out, stream);
+  if (err == hipSuccess)
+    err = fuse ? launch_expert_gemm2_fused(h, offsets, w_down, H, I, E_local, cap, row_info, out,
+                                           static_cast<uint16_t*>(y), stream)
+               : launch_expert_gemm2(h, offsets, w_down, H, I, E_local, cap, out, stream);
   if (err == hipSuccess) err = mark(4);
-  if (err == hipSuccess) err = launch_combine(out, inv, topk_w, T, H, k, y, y_f32, stream);
+  if (err == hipSuccess) err = launch_combine(out, inv, topk_w, T, H, k, y, y_f32, stream, fuse);
   if (err == hipSuccess) err = mark(5);
   return hip_status(err);
 }
@@ -271,6 +280,24 @@ int moe_forward_profiled(const moe_bf16* x, const float* w_router, const float* 
     if (!events[i]) return MOE_ERR_INVALID_ARG;
   return forward_impl(x, w_router, bias, w_gate_up, w_down, T, H, I, E, k, e0, E_local, renormalize, y, false,
                       workspace, workspace_bytes, events, stream);
+}
+
+int moe_forward_fused(const moe_bf16* x, const float* w_router, const float* bias, const moe_bf16* w_gate_up,
+                      const moe_bf16* w_down, int T, int H, int I, int E, int k, int e0, int E_local,
+                      int renormalize, moe_bf16* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return forward_impl(x, w_router, bias, w_gate_up, w_down, T, H, I, E, k, e0, E_local, renormalize, y, false,
+                      workspace, workspace_bytes, nullptr, stream, true);
+}
+
+int moe_forward_fused_profiled(const moe_bf16* x, const float* w_router, const float* bias,
+                               const moe_bf16* w_gate_up, const moe_bf16* w_down, int T, int H, int I, int E, int k,
+                               int e0, int E_local, int renormalize, moe_bf16* y, void* workspace,
+                               size_t workspace_bytes, hipEvent_t* events, hipStream_t stream) {
+  if (!events) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < 6; ++i)
+    if (!events[i]) return MOE_ERR_INVALID_ARG;
+  return forward_impl(x, w_router, bias, w_gate_up, w_down, T, H, I, E, k, e0, E_local, renormalize, y, false,
+                      workspace, workspace_bytes, events, stream, true);
 }
 
 }  // extern "C"

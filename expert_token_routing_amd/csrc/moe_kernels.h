@@ -47,6 +47,21 @@ hipError_t launch_expert_gemm1_gather(const uint16_t* x, const int32_t* perm_src
                                       const uint16_t* w_gate_up, int H, int I, int E_local, int64_t capacity,
                                       uint16_t* h, hipStream_t stream);
 
+// Down GEMM with the combine of single-selection tokens in its epilogue:
+// row_info[n] = {token, bits of its combine weight} when row n's token has
+// exactly one local selection, else {-1, 0}; such rows are written to y [T, H]
+// as w * out (rounded as the combine rounds a one-term sum), the others to
+// out. Usable when expert_gemm2_can_fuse(I).
+bool expert_gemm2_can_fuse(int I);
+hipError_t launch_expert_gemm2_fused(const uint16_t* h, const int32_t* offsets, const uint16_t* w_down, int H, int I,
+                                     int E_local, int64_t capacity, const int2* row_info, uint16_t* out, uint16_t* y,
+                                     hipStream_t stream);
+
+// row_info of launch_expert_gemm2_fused from inv and topk_w (one thread per
+// token); rows of tokens with two or more local selections get {-1, 0}.
+hipError_t launch_single_rows(const int32_t* inv, const float* topk_w, int T, int k, int2* row_info,
+                              hipStream_t stream);
+
 // Bytes of the dispatch tables in the workspace: the per-chunk histogram
 // table [E][ceil(T/64)] i32, then the per-chunk lane sets (at most E per
 // chunk) u64.
@@ -57,9 +72,11 @@ hipError_t launch_dispatch_index(const int32_t* topk_idx, int T, int E, int k, i
                                  int32_t* offsets, int32_t* perm_src, int32_t* inv, int32_t* chunk_table,
                                  hipStream_t stream);
 
-// Weighted top-k sum in token order; y is bf16, or float32 when y_f32.
+// Weighted top-k sum in token order; y is bf16, or float32 when y_f32. With
+// skip_single, tokens with exactly one local selection are left untouched
+// (the fused down GEMM wrote them; bf16 y only).
 hipError_t launch_combine(const uint16_t* expert_out, const int32_t* inv, const float* topk_w, int T, int H, int k,
-                          void* y, bool y_f32, hipStream_t stream);
+                          void* y, bool y_f32, hipStream_t stream, bool skip_single = false);
 
 // Cached device facts of the current device.
 int device_cu_count();

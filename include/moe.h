@@ -243,6 +243,36 @@ int moe_forward_profiled(const moe_bf16* x, const float* w_router, const float* 
                          hipStream_t stream);
 
 /*
+ * moe_forward with the combine fused into the down-projection GEMM where it
+ * needs no reduction across expert tiles. A token's local selections sit in
+ * different expert segments, so summing them inside the GEMM would need
+ * float atomics across the chip's L2 domains (and lose the fixed slot
+ * order); a token with exactly one local selection needs no sum: its y row
+ * is w * out, and the down GEMM's epilogue writes it straight to y in token
+ * order ("EP: Partition Experts and Route Tokens", "Return multiple expert
+ * results to the same token": the weighted return of an expert's result to
+ * its token). The combine kernel then sums only tokens with two or more local
+ * selections and zero-fills those with none. The epilogue rounds exactly as
+ * the separate combine rounds a one-term sum, so y equals moe_forward's y
+ * bit for bit. Arguments, workspace size and checks are moe_forward's; where
+ * the down GEMM's k extent I is not a multiple of 32 the separate path runs.
+ */
+int moe_forward_fused(const moe_bf16* x, const float* w_router, const float* bias,
+                      const moe_bf16* w_gate_up, const moe_bf16* w_down, int T, int H, int I, int E,
+                      int k, int e0, int E_local, int renormalize, moe_bf16* y, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_forward_fused with the timing marks of moe_forward_profiled (the
+ * single-selection table is built between the second and third marks).
+ */
+int moe_forward_fused_profiled(const moe_bf16* x, const float* w_router, const float* bias,
+                               const moe_bf16* w_gate_up, const moe_bf16* w_down, int T, int H, int I,
+                               int E, int k, int e0, int E_local, int renormalize, moe_bf16* y,
+                               void* workspace, size_t workspace_bytes, hipEvent_t* events,
+                               hipStream_t stream);
+
+/*
  * Byte offsets of the intermediates inside the moe_forward workspace, so a
  * caller can read them after the call (for checks and measurements). Writes
  * 9 values into `offsets_out` (host memory): logits, topk_idx, topk_w, counts,

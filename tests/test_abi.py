@@ -156,6 +156,6 @@ def _forward(name="moe_forward", **kw):
     (dict(k=0), M.MOE_ERR_INVALID_ARG),
     (dict(T=0, x=None, y=None), M.MOE_OK),
 ])
-@pytest.mark.parametrize("name", ["moe_forward", "moe_forward_f32"])
+@pytest.mark.parametrize("name", ["moe_forward", "moe_forward_f32", "moe_forward_fused"])
 def test_forward_rejects(name, kw, want):
     assert _forward(name, **kw) == want

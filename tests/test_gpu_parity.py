@@ -89,6 +89,19 @@ def run_steps(d: DevInputs):
     return res
 
 
+def check_fused_forward(d: DevInputs, y_ref: torch.Tensor) -> None:
+    """moe_forward_fused (single-selection tokens combined in the down GEMM's
+    epilogue) gives the separate combine's bits; y starts as NaN, so a row
+    that neither the epilogue nor the combine wrote would show."""
+    cfg = d.cfg
+    say(f"moe_forward_fused {cfg.name}")
+    y = torch.full((cfg.T, cfg.H), float("nan"), dtype=torch.bfloat16, device=d.x.device)
+    M.moe_forward_fused(d.x, d.w_router, d.bias, d.w_gate_up, d.w_down, cfg.k, cfg.e0, cfg.renormalize, y=y)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), \
+        int((y.view(torch.int16) != y_ref.view(torch.int16)).sum())
+
+
 def check_route(cfg, inp, logits, idx, w):
     """Logits within float32 accuracy of the float64 definition; selection
     and weights exactly / tightly equal to the oracle's on the same logits."""
@@ -218,11 +231,12 @@ def test_small_case_all_steps(cfg):
     y_ref = O.oracle_forward(inp.x, inp.w_router, inp.bias, inp.w_gate_up, inp.w_down, cfg.k, cfg.e0,
                              cfg.E_local, cfg.renormalize, logits=gl)
     assert rel_max_err(bf16_f64(res["y"]), y_ref) <= OUT_TOL
-    # the fused entry point gives the same bits as the four steps
+    # the whole-share entry point gives the same bits as the four steps
     say(f"moe_forward {cfg.name}")
     y, _ = M.moe_forward(d.x, d.w_router, d.bias, d.w_gate_up, d.w_down, cfg.k, cfg.e0, cfg.renormalize)
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), res["y"].view(torch.int16))
+    check_fused_forward(d, res["y"])
 
 
 def test_identity_experts_return_tokens_unchanged():
@@ -398,6 +412,7 @@ def test_named_workload_full_size(name):
     y, _ = M.moe_forward(d.x, d.w_router, d.bias, d.w_gate_up, d.w_down, cfg.k, cfg.e0, cfg.renormalize)
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), res["y"].view(torch.int16))
+    check_fused_forward(d, res["y"])
     # sampled tokens end to end against the oracle's definition
     toks = rng.choice(cfg.T, size=min(cfg.T, 48), replace=False)
     yref = np.zeros((toks.size, cfg.H))
