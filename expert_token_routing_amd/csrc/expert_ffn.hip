@@ -197,7 +197,9 @@ __device__ __forceinline__ void alternate_mfma_reads() {
 // token and combine weight of a row whose token has exactly one local
 // selection (token -1 otherwise); such rows go to y as the combine would
 // write them, the others to C.
-template <int FMT, bool SWIGLU, bool FUSE, typename SrcRow, typename ColOf>
+// HALF: K % 64 == 32, so the last stage holds half a stage of k values; its
+// loads then stay inside the operands (issue_half).
+template <int FMT, bool SWIGLU, bool FUSE, bool HALF, typename SrcRow, typename ColOf>
 __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __restrict__ Abase, int64_t a_bytes,
                                          int lda, int rows, SrcRow src_row, const uint16_t* __restrict__ We, int ldw,
                                          int K, ColOf col_of, int out_c0, int N, uint16_t* __restrict__ C, int ldc,
@@ -237,8 +239,13 @@ __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __re
   auto issue = [&](int st) {
     if (st < nk) {
       const int buf = st % kStages;
-      la.issue(ldsA + buf * kAStage, st * kSK);
-      lb.issue(ldsB + buf * kBStage, st);
+      if (HALF && st == nk - 1) {
+        la.issue_half(ldsA + buf * kAStage, st * kSK);
+        lb.issue_half(ldsB + buf * kBStage, st);
+      } else {
+        la.issue(ldsA + buf * kAStage, st * kSK);
+        lb.issue(ldsB + buf * kBStage, st);
+      }
     }
   };
   // Wait until stage s landed, then barrier. Stages complete in issue order;
@@ -398,7 +405,7 @@ __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __re
 // FUSE (down GEMM): row_info[n] = {token, combine weight bits} for row n of a
 // token with exactly one local selection, {-1, 0} otherwise; those rows are
 // written to y [T, ldc] instead of C.
-template <bool SWIGLU, bool FUSE = false>
+template <bool SWIGLU, bool FUSE, bool HALF>
 __global__ void __launch_bounds__(dma::kThreads)
 panel_gemm_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __restrict__ offsets, int E_local,
                   int64_t capacity, const uint16_t* __restrict__ W, int64_t w_expert_stride, int ldw,
@@ -543,11 +550,11 @@ panel_gemm_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __rest
     auto go = [&](auto fm_t) {
       constexpr int FMT = decltype(fm_t)::value;
       if (gather_src != nullptr) {
-        panelffn::run_tile<FMT, SWIGLU, FUSE>(lds, A, int64_t(gather_rows) * lda * 2, lda, rows,
+        panelffn::run_tile<FMT, SWIGLU, FUSE, HALF>(lds, A, int64_t(gather_rows) * lda * 2, lda, rows,
                                               [&](int r) { return gather_src[r0 + r] / gather_k; }, We, ldw, K,
                                               col_of, out_c0, N, C, ldc, r0, (const MOE_LDS int*)ri_buf, y);
       } else {
-        panelffn::run_tile<FMT, SWIGLU, FUSE>(lds, A + int64_t(r0) * lda, int64_t(rows) * lda * 2, lda, rows,
+        panelffn::run_tile<FMT, SWIGLU, FUSE, HALF>(lds, A + int64_t(r0) * lda, int64_t(rows) * lda * 2, lda, rows,
                                               [](int r) { return r; }, We, ldw, K, col_of, out_c0, N, C, ldc, r0,
                                               (const MOE_LDS int*)ri_buf, y);
       }
@@ -580,13 +587,25 @@ unsigned dma_grid(int64_t tiles) {
   return unsigned(want);
 }
 
+// The panel kernel for k extent K (HALF when K ends in half a 64-deep stage).
+template <bool SWIGLU, bool FUSE>
+hipError_t launch_panel(int64_t tiles, hipStream_t stream, const uint16_t* A, int lda, const int32_t* offsets,
+                        int E_local, int64_t capacity, const uint16_t* W, int64_t w_expert_stride, int ldw,
+                        uint16_t* C, int ldc, int K, int N, int up_off, const int32_t* gather_src, int gather_k,
+                        int gather_rows, const int2* row_info, uint16_t* y) {
+  const bool half = K % dma::panel::kSK != 0;
+  auto* kern = half ? panel_gemm_kernel<SWIGLU, FUSE, true> : panel_gemm_kernel<SWIGLU, FUSE, false>;
+  hipLaunchKernelGGL(kern, dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream, A, lda, offsets, E_local, capacity,
+                     W, w_expert_stride, ldw, C, ldc, K, N, up_off, gather_src, gather_k, gather_rows, row_info, y);
+  return hipGetLastError();
+}
+
 hipError_t launch_expert_gemm1(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_gate_up, int H,
                                int I, int E_local, int64_t capacity, uint16_t* h, hipStream_t stream) {
   if (H % dma::kBK == 0) {
     const int64_t tiles = (ceil_div(capacity, kRowCapMin) + E_local) * ceil_div(I, dma::panel::kBN / 2);
-    hipLaunchKernelGGL((panel_gemm_kernel<true>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream, x_perm, H,
-                       offsets, E_local, capacity, w_gate_up, int64_t(H) * 2 * I, 2 * I, h, I, H, I, I, nullptr, 1, 0, nullptr, nullptr);
-    return hipGetLastError();
+    return launch_panel<true, false>(tiles, stream, x_perm, H, offsets, E_local, capacity, w_gate_up,
+                                     int64_t(H) * 2 * I, 2 * I, h, I, H, I, I, nullptr, 1, 0, nullptr, nullptr);
   }
   const int64_t mt_bound = ceil_div(capacity, kFfnBM) + E_local;
   const unsigned grid = persistent_grid(mt_bound * ceil_div(I, 128));
@@ -599,9 +618,8 @@ hipError_t launch_expert_gemm2(const uint16_t* h, const int32_t* offsets, const 
                                int E_local, int64_t capacity, uint16_t* out, hipStream_t stream) {
   if (I % dma::kBK == 0) {
     const int64_t tiles = (ceil_div(capacity, kRowCapMin) + E_local) * ceil_div(H, dma::panel::kBN);
-    hipLaunchKernelGGL((panel_gemm_kernel<false>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream, h, I,
-                       offsets, E_local, capacity, w_down, int64_t(I) * H, H, out, H, I, H, 0, nullptr, 1, 0, nullptr, nullptr);
-    return hipGetLastError();
+    return launch_panel<false, false>(tiles, stream, h, I, offsets, E_local, capacity, w_down, int64_t(I) * H, H,
+                                      out, H, I, H, 0, nullptr, 1, 0, nullptr, nullptr);
   }
   const int64_t mt_bound = ceil_div(capacity, kFfnBM) + E_local;
   const unsigned grid = persistent_grid(mt_bound * ceil_div(H, 256));
@@ -616,10 +634,8 @@ hipError_t launch_expert_gemm2_fused(const uint16_t* h, const int32_t* offsets, 
                                      int E_local, int64_t capacity, const int2* row_info, uint16_t* out, uint16_t* y,
                                      hipStream_t stream) {
   const int64_t tiles = (ceil_div(capacity, kRowCapMin) + E_local) * ceil_div(H, dma::panel::kBN);
-  hipLaunchKernelGGL((panel_gemm_kernel<false, true>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream, h, I,
-                     offsets, E_local, capacity, w_down, int64_t(I) * H, H, out, H, I, H, 0, nullptr, 1, 0, row_info,
-                     y);
-  return hipGetLastError();
+  return launch_panel<false, true>(tiles, stream, h, I, offsets, E_local, capacity, w_down, int64_t(I) * H, H, out,
+                                   H, I, H, 0, nullptr, 1, 0, row_info, y);
 }
 
 bool expert_gemm1_can_gather(int T, int H) { return H % dma::kBK == 0 && int64_t(T) * H * 2 < (int64_t(1) << 31); }
@@ -628,10 +644,8 @@ hipError_t launch_expert_gemm1_gather(const uint16_t* x, const int32_t* perm_src
                                       const uint16_t* w_gate_up, int H, int I, int E_local, int64_t capacity,
                                       uint16_t* h, hipStream_t stream) {
   const int64_t tiles = (ceil_div(capacity, kRowCapMin) + E_local) * ceil_div(I, dma::panel::kBN / 2);
-  hipLaunchKernelGGL((panel_gemm_kernel<true>), dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream, x, H, offsets,
-                     E_local, capacity, w_gate_up, int64_t(H) * 2 * I, 2 * I, h, I, H, I, I, perm_src, k, T, nullptr,
-                     nullptr);
-  return hipGetLastError();
+  return launch_panel<true, false>(tiles, stream, x, H, offsets, E_local, capacity, w_gate_up, int64_t(H) * 2 * I,
+                                   2 * I, h, I, H, I, I, perm_src, k, T, nullptr, nullptr);
 }
 
 hipError_t launch_expert_ffn(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_gate_up,

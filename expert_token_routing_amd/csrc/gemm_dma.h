@@ -258,6 +258,24 @@ struct ALoaderP {
     for (int i = 0; i < kPerMax; ++i)
       if (i < count) dma16(rsrc, voff[i], 2u * uint32_t(k0), As + 1024 * (i * kWaves + w));
   }
+  // A stage whose k range holds only its first 32 values (the end of K): the
+  // lanes of the second half read the first half again instead, so no
+  // request reaches past a row's end (the extra k values are multiplied as
+  // zeros). A lane's logical chunk is (lane % 8) ^ ((4 w + lane / 16) % 8)
+  // for every load i: the row of load i is 64 i + 8 w + lane / 8, and 64 i
+  // does not change the swizzle bits.
+  __device__ __forceinline__ void issue_half(MOE_LDS char* As, int k0) const {
+    static_assert(kSK == 64 && kRowsPerLoad == 8 && kWaves == 8, "chunk of a lane independent of the load");
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = lane_id();
+    uint32_t back = ((lane & 7) ^ ((4 * w + (lane >> 4)) & 7)) >= 4 ? 64u : 0u;
+    // opaque here, so the adjusted offsets are formed only when this runs
+    // (once per tile) instead of being kept in registers across the k loop
+    asm volatile("" : "+v"(back));
+#pragma unroll
+    for (int i = 0; i < kPerMax; ++i)
+      if (i < count) dma16(rsrc, voff[i] - back, 2u * uint32_t(k0), As + 1024 * (i * kWaves + w));
+  }
 };
 
 // B stage: kSK k x kBN columns of an n-contiguous matrix, 4 x 16 blocks of
@@ -286,6 +304,16 @@ struct BLoaderP {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) dma16(rsrc, voff[j], uint32_t(stage) * stage_bytes, Bs + 1024 * (j * kWaves + w));
+  }
+  // A stage holding only k rows 0..31 (the end of K): loads j >= kPer / 2
+  // (k rows 32..63, see init) read rows 0..31 again, so none reaches past the
+  // matrix; those k values are multiplied as zeros.
+  __device__ __forceinline__ void issue_half(MOE_LDS char* Bs, int stage) const {
+    static_assert(kSK == 64 && kNQ == 16 && kPer == 4, "loads 0, 1 hold k rows 0..31");
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      dma16(rsrc, voff[j % (kPer / 2)], uint32_t(stage) * stage_bytes, Bs + 1024 * (j * kWaves + w));
   }
 };
 
