@@ -33,7 +33,7 @@ STAGES = ["route", "dispatch", "gemm1_gate_up_swiglu", "gemm2_down", "combine"]
 COUNTERS_MD = os.path.join(ROOT, "profiles", "gemm1_dsr1_ep8_share_counters.md")
 GEMM1_SOURCES = ["expert_token_routing_amd/csrc/expert_ffn.hip", "expert_token_routing_amd/csrc/gemm_dma.h",
                  "expert_token_routing_amd/csrc/gemm_tile.h", "expert_token_routing_amd/csrc/moe_device.h"]
-GEMM1_KERNEL = "panel_gemm_kernel<true>"
+GEMM1_KERNEL = "panel_gemm_kernel<true, false, false>"
 
 
 def log(*a):
@@ -115,7 +115,7 @@ def summarize_counters(fetch_dir, write_dir, command):
     f_kib, w_kib = sum(g_f) / len(g_f), sum(g_w) / len(g_w)
     traffic = (f_kib * f_scale + w_kib * w_scale) * 1024.0
     lines = [
-        "# HBM traffic of the gate/up GEMM (panel_gemm_kernel<true>), DeepSeek-R1-shaped share",
+        "# HBM traffic of the gate/up GEMM (panel_gemm_kernel<true, false, false>), DeepSeek-R1-shaped share",
         "",
         "Two counter runs (FETCH_SIZE, then WRITE_SIZE) of the command below; the calibration copy of "
         f"{mib} MiB device to device reads {copy_f:.0f} KiB as FETCH_SIZE and {copy_w:.0f} KiB as WRITE_SIZE, "
