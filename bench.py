@@ -363,6 +363,7 @@ def main():
     wall = time.perf_counter() - t0
     stage_ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(5)] for i in range(args.steps)])
     stage_avg = stage_ms.mean(0)
+    step_ev = stage_ms.sum(1)  # per-step device time between the first and last event
     log("[bench] stage ms: " + ", ".join(f"{n}={v:.3f}" for n, v in zip(STAGES, stage_avg)))
 
     cold = None
@@ -527,6 +528,10 @@ def main():
                     "the down GEMM's epilogue, the combine kernel sums the rest; y is bit-identical to "
                     "moe_forward's"},
         "layer_tflops": round(total_flop / (ms_per_step * 1e-3) / 1e12, 2),
+        "step_ms_events": {"p10": round(float(np.percentile(step_ev, 10)), 4),
+                           "p50": round(float(np.percentile(step_ev, 50)), 4),
+                           "p90": round(float(np.percentile(step_ev, 90)), 4),
+                           "note": "per-step device time from the stage events of the timed steps"},
         "realised": {"N_local_rows": N, "U_tokens_with_local_pick": U,
                      "rows_per_local_expert_max": int(np.diff(offs).max()),
                      "local_experts_empty": int((np.diff(offs) == 0).sum())},
