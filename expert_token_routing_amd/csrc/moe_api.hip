@@ -49,6 +49,10 @@ static int check_local(int E, int e0, int E_local) {
   return MOE_OK;
 }
 static int64_t min_capacity(int T, int k, int E_local) { return int64_t(T) * std::min(k, E_local); }
+// The GEMMs address one expert's weight matrix through a buffer resource
+// whose range and offsets are 32-bit: gate_up (H x 2I bf16, the larger of the
+// two) must stay below 2 GiB, i.e. H * I < 2^29.
+static bool expert_weights_fit(int H, int I) { return int64_t(H) * I * 4 < (int64_t(1) << 31); }
 static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // Workspace layout of moe_forward.
@@ -93,7 +97,7 @@ const char* moe_status_string(int status) {
   switch (status) {
     case MOE_OK: return "MOE_OK";
     case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid size, index range or null pointer";
-    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: outside the supported sizes (E <= 1024, k <= 32, T*k < 2^31)";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: outside the supported sizes (E <= 1024, k <= 32, T*k < 2^31, H*I < 2^29)";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch failed";
     default: return "unknown moe_status";
@@ -152,7 +156,7 @@ int moe_expert_ffn(const moe_bf16* x_perm, const int32_t* offsets, const moe_bf1
                    const moe_bf16* w_down, int H, int I, int E_local, int64_t capacity, moe_bf16* h,
                    moe_bf16* out, hipStream_t stream) {
   if (H <= 0 || I <= 0 || (H % 8) != 0 || (I % 8) != 0 || E_local < 1 || capacity < 0) return MOE_ERR_INVALID_ARG;
-  if (E_local > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (E_local > kMaxE || !expert_weights_fit(H, I)) return MOE_ERR_UNSUPPORTED;
   if (capacity >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   if (capacity == 0) return MOE_OK;
   if (!x_perm || !offsets || !w_gate_up || !w_down || !h || !out) return MOE_ERR_INVALID_ARG;
@@ -202,6 +206,7 @@ static int forward_impl(const moe_bf16* x, const float* w_router, const float* b
   if (st != MOE_OK) return st;
   if ((st = check_local(E, e0, E_local)) != MOE_OK) return st;
   if (I <= 0 || (I % 8) != 0) return MOE_ERR_INVALID_ARG;
+  if (!expert_weights_fit(H, I)) return MOE_ERR_UNSUPPORTED;
   if (min_capacity(T, k, E_local) >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !w_router || !w_gate_up || !w_down || !y) return MOE_ERR_INVALID_ARG;

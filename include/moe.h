@@ -35,7 +35,8 @@
  *     has reached the call's point.
  *   - T = 0 is valid: the call returns MOE_OK and launches nothing.
  *   - supported sizes: 1 <= k <= min(E, 32); E <= 1024; H and I multiples
- *     of 8 (16-byte vectors); T * k < 2^31.
+ *     of 8 (16-byte vectors); T * k < 2^31; H * I < 2^29 (one expert's
+ *     gate_up matrix below 2 GiB), else MOE_ERR_UNSUPPORTED.
  *   - matrix pointers (x, w_router, w_gate_up, w_down, x_perm, h, out,
  *     expert_out, y) are 16-byte aligned; a misaligned one is
  *     MOE_ERR_INVALID_ARG.

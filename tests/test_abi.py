@@ -114,6 +114,8 @@ def test_dispatch_rejects(kw, want):
     ((FAKE, FAKE, FAKE, FAKE, 12, 8, 2, 16, FAKE, FAKE, None), M.MOE_ERR_INVALID_ARG),     # H % 8
     ((FAKE, FAKE, FAKE, FAKE, 8, 4, 2, 16, FAKE, FAKE, None), M.MOE_ERR_INVALID_ARG),      # I % 8
     ((FAKE, FAKE, FAKE, FAKE, 8, 8, 2000, 16, FAKE, FAKE, None), M.MOE_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, FAKE, 16384, 32768, 2, 16, FAKE, FAKE, None), M.MOE_ERR_UNSUPPORTED),  # gate_up >= 2 GiB
+    ((FAKE, FAKE, FAKE, FAKE, 16384, 32760, 2, 16, FAKE, None, None), M.MOE_ERR_INVALID_ARG),  # just below: h checked
     ((FAKE, None, FAKE, FAKE, 8, 8, 2, 16, FAKE, FAKE, None), M.MOE_ERR_INVALID_ARG),
     ((FAKE, FAKE, FAKE, FAKE_ODD, 8, 8, 2, 16, FAKE, FAKE, None), M.MOE_ERR_INVALID_ARG),
     ((None, None, None, None, 8, 8, 2, 0, None, None, None), M.MOE_OK),                    # no rows
@@ -154,6 +156,7 @@ def _forward(name="moe_forward", **kw):
     (dict(wsb=1024), M.MOE_ERR_WORKSPACE),
     (dict(ws=None), M.MOE_ERR_WORKSPACE),
     (dict(k=0), M.MOE_ERR_INVALID_ARG),
+    (dict(H=16384, I=32768), M.MOE_ERR_UNSUPPORTED),  # one expert's gate_up matrix >= 2 GiB
     (dict(T=0, x=None, y=None), M.MOE_OK),
 ])
 @pytest.mark.parametrize("name", ["moe_forward", "moe_forward_f32", "moe_forward_fused"])
