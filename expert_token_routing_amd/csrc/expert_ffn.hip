@@ -405,12 +405,15 @@ __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __re
 // FUSE (down GEMM): row_info[n] = {token, combine weight bits} for row n of a
 // token with exactly one local selection, {-1, 0} otherwise; those rows are
 // written to y [T, ldc] instead of C.
+// Experts with at most skip_rows rows get no tiles (the grouped GEMV runs
+// them).
 template <bool SWIGLU, bool FUSE, bool HALF>
 __global__ void __launch_bounds__(dma::kThreads)
 panel_gemm_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __restrict__ offsets, int E_local,
                   int64_t capacity, const uint16_t* __restrict__ W, int64_t w_expert_stride, int ldw,
                   uint16_t* __restrict__ C, int ldc, int K, int N, int up_off, const int32_t* __restrict__ gather_src,
-                  int gather_k, int gather_rows, const int2* __restrict__ row_info, uint16_t* __restrict__ y) {
+                  int gather_k, int gather_rows, const int2* __restrict__ row_info, uint16_t* __restrict__ y,
+                  int skip_rows) {
   using namespace dma::panel;
   static_assert(!(FUSE && SWIGLU), "the combine is fused into the down GEMM only");
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
@@ -437,7 +440,7 @@ panel_gemm_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __rest
       const int64_t a = min<int64_t>(max<int64_t>(offsets[i], 0), capacity);
       const int64_t b = max<int64_t>(a, min<int64_t>(offsets[i + 1], capacity));
       s_off[i] = int(a);
-      me[q] = int(b - a);
+      me[q] = b - a > skip_rows ? int(b - a) : 0;
       if (i == E_local - 1) s_off[E_local] = int(b);
     }
   }
@@ -593,10 +596,24 @@ hipError_t launch_panel(int64_t tiles, hipStream_t stream, const uint16_t* A, in
                         int E_local, int64_t capacity, const uint16_t* W, int64_t w_expert_stride, int ldw,
                         uint16_t* C, int ldc, int K, int N, int up_off, const int32_t* gather_src, int gather_k,
                         int gather_rows, const int2* row_info, uint16_t* y) {
+  // With few rows per expert on average, the experts with at most
+  // grouped_gemv_max_rows() rows go to the grouped GEMV and the tiles take
+  // the rest (none can have more when the capacity is that small).
+  int skip_rows = 0;
+  if (grouped_gemv_usable(capacity, E_local, K)) {
+    const hipError_t err =
+        SWIGLU ? launch_grouped_gemv1(A, lda, gather_src, gather_k, gather_rows, offsets, E_local, capacity, W, K,
+                                      N, C, stream)
+               : launch_grouped_gemv2(A, offsets, E_local, capacity, W, N, K, row_info, C, y, stream);
+    if (err != hipSuccess) return err;
+    skip_rows = grouped_gemv_max_rows();
+    if (capacity <= skip_rows) return hipSuccess;
+  }
   const bool half = K % dma::panel::kSK != 0;
   auto* kern = half ? panel_gemm_kernel<SWIGLU, FUSE, true> : panel_gemm_kernel<SWIGLU, FUSE, false>;
   hipLaunchKernelGGL(kern, dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream, A, lda, offsets, E_local, capacity,
-                     W, w_expert_stride, ldw, C, ldc, K, N, up_off, gather_src, gather_k, gather_rows, row_info, y);
+                     W, w_expert_stride, ldw, C, ldc, K, N, up_off, gather_src, gather_k, gather_rows, row_info, y,
+                     skip_rows);
   return hipGetLastError();
 }
 

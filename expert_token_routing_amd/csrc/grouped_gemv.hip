@@ -1,0 +1,269 @@
+// Grouped GEMV: the expert MLPs when each expert holds only a few token rows.
+//
+// In a decode step every rank runs all tokens through its local experts
+// ("Expert Parallelism (EP)", "Collective Patterns / Decode (TKG kernel)"),
+// and a batch of a few hundred tokens leaves each expert a handful of rows.
+// The two GEMMs then do a few flops per weight byte and are bound by
+// streaming the local experts' weights from HBM.
+//
+// No LDS is used: every wave streams its own weight panel straight into
+// registers, D k-steps ahead of the matrix cores.
+//
+// Wave geometry. A wave owns one panel of 16 CPL weight columns of one expert
+// (CPL = 4 or 8 columns per lane) and walks k in steps of 32. Lane l = 16 g + m
+// loads, per step, CPL columns (2 CPL bytes) from each of the 8 weight rows
+// k0 + 8 g .. k0 + 8 g + 7, and the 16 bytes of token row m at the same 8 k.
+// Transposing its 8 x CPL block in registers gives the lane, for each of its
+// columns c, the 8 k-values that lane (g, m) of a v_mfma_f32_16x16x32_bf16 A
+// operand holds for A row m. So MFMA c multiplies the 16 columns
+// colbase(m) + c (A rows m = 0..15) by the token rows (B columns m), and CPL
+// MFMAs per step cover the panel. Afterwards lane (g, m) holds, in
+// accumulator c, element v, column colbase(4 g + v) + c of token row m.
+//
+// Panel columns. Down GEMM: the panel is 16 CPL consecutive output columns,
+// colbase(m) = CPL m, so a lane ends with the 4 CPL consecutive columns
+// from 4 CPL g. Gate/up GEMM: the panel is 8 CPL outputs o0 .. with their gate
+// and up columns side by side: colbase(4 g' + v') is gate column
+// o0 + 2 CPL g' + CPL v' (v' < 2) or the up column of o0 + 2 CPL g' +
+// CPL (v' - 2) (v' >= 2), so a lane ends with the gate (v = 0, 1) and up
+// (v = 2, 3) values of its 2 CPL consecutive outputs from o0 + 2 CPL g. With
+// CPL = 8 the 16 lanes of a group read whole 128-byte lines of gate and of
+// up per weight row.
+//
+// Every output element is one MFMA chain over k in steps of 32 from k = 0,
+// with the weights as the A operand, as in the tile kernel's gate/up GEMM.
+#include <type_traits>
+#include <utility>
+
+#include "gemm_dma.h"
+#include "moe_kernels.h"
+
+namespace moe {
+namespace gemv {
+
+using dma::panel::f32x4v;
+using dma::panel::mfma16x16x32;
+
+constexpr int kWaves = 4;             // waves per workgroup (independent)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStepK = 32;            // k per step
+constexpr int kMaxRows = 16;          // token rows of one expert a wave handles
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  // bytes < 2^31 on every path (checked by the callers)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
+}
+
+// Loads of one step: 8 weight rows x CPL columns, and the token row's 8 k.
+template <int D, int CPL>
+struct Ring {
+  typedef typename std::conditional<CPL == 8, u32x4, u32x2>::type WRow;
+  WRow w[D][8];
+  u32x4 x[D];
+};
+
+// WAUX: cache policy of the weight loads (2: non-temporal; each weight byte
+// is read once)
+template <bool SWIGLU, bool FUSE, int D, int CPL, int WAUX>
+__global__ void __launch_bounds__(kThreads)
+grouped_gemv_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __restrict__ gather_src, int gather_k,
+                    int gather_rows, const int32_t* __restrict__ offsets, int E_local, int64_t capacity,
+                    const uint16_t* __restrict__ W, int64_t w_expert_stride, int ldw, int K, int N, int up_off,
+                    uint16_t* __restrict__ C, int ldc, const int2* __restrict__ row_info, uint16_t* __restrict__ y) {
+  static_assert(!(FUSE && SWIGLU), "the combine is fused into the down GEMM only");
+  static_assert(D >= 1 && 9 * (D - 1) <= 63, "loads in flight must fit the vmcnt counter");
+  static_assert(CPL == 4 || CPL == 8, "4 or 8 columns per lane");
+  constexpr int kOut = SWIGLU ? 8 * CPL : 16 * CPL;  // outputs per panel
+  const int npanel = (N + kOut - 1) / kOut;
+  const int wave = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * kWaves + int(threadIdx.x >> 6));
+  const int e = wave / npanel;
+  if (e >= E_local) return;
+  const int p = wave - e * npanel;
+  const int64_t a0 = min<int64_t>(max<int64_t>(offsets[e], 0), capacity);
+  const int64_t b0 = max<int64_t>(a0, min<int64_t>(offsets[e + 1], capacity));
+  const int rows = __builtin_amdgcn_readfirstlane(int(b0 - a0));
+  // experts with more rows run in the tile kernel
+  if (rows == 0 || rows > kMaxRows) return;
+  const int r0 = __builtin_amdgcn_readfirstlane(int(a0));
+
+  const int lane = lane_id();
+  const int g = lane >> 4, m = lane & 15;
+
+  // this lane's CPL weight columns (N is a multiple of 8: a block of CPL
+  // columns is wholly inside or wholly past the end)
+  int col;
+  if (SWIGLU) {
+    const int o = kOut * p + 2 * CPL * (m >> 2) + CPL * (m & 1);
+    col = o < N ? ((m & 2) ? up_off + o : o) : 0;
+  } else {
+    const int c = kOut * p + CPL * m;
+    col = c < N ? c : 0;
+  }
+  const rsrc_t wr = make_rsrc(W + int64_t(e) * w_expert_stride, int64_t(K) * ldw * 2);
+  const uint32_t wvo = uint32_t(8 * g * ldw + col) * 2u;
+  const int wrow = ldw * 2;  // bytes per weight row
+
+  // token row m (the last row again past the expert's rows)
+  const int rm = min(m, rows - 1);
+  rsrc_t xr;
+  uint32_t xvo;
+  if (gather_src != nullptr) {
+    xr = make_rsrc(A, int64_t(gather_rows) * lda * 2);
+    xvo = uint32_t(gather_src[r0 + rm] / gather_k) * uint32_t(lda) * 2u + 16u * uint32_t(g);
+  } else {
+    xr = make_rsrc(A + int64_t(r0) * lda, int64_t(rows) * lda * 2);
+    xvo = uint32_t(rm) * uint32_t(lda) * 2u + 16u * uint32_t(g);
+  }
+
+  const int nsteps = K / kStepK;
+  Ring<D, CPL> q;
+  // step s (clamped to the last one, so every lane issues the same loads)
+  auto load = [&](auto d_t, int s) {
+    constexpr int d = decltype(d_t)::value;
+    s = min(s, nsteps - 1);
+    const int so = s * kStepK * wrow;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      if constexpr (CPL == 8)
+        q.w[d][r] = __builtin_amdgcn_raw_buffer_load_b128(wr, wvo, so + r * wrow, WAUX);
+      else
+        q.w[d][r] = __builtin_amdgcn_raw_buffer_load_b64(wr, wvo, so + r * wrow, WAUX);
+    }
+    q.x[d] = __builtin_amdgcn_raw_buffer_load_b128(xr, xvo, s * kStepK * 2, 0);
+    // keep the slots' loads in slot order: the wait before a slot is used
+    // counts the loads of the slots issued after it
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  f32x4v acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = f32x4v{0.f, 0.f, 0.f, 0.f};
+  auto consume = [&](auto d_t) {
+    constexpr int d = decltype(d_t)::value;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      // column c of the 8 x 4 block: dword j = rows 2j (low half), 2j+1
+      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 a;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = __builtin_amdgcn_perm(q.w[d][2 * j + 1][c >> 1], q.w[d][2 * j][c >> 1], sel);
+      acc[c] = mfma16x16x32(a, q.x[d], acc[c]);
+    }
+  };
+
+  static_for<D>([&](auto d_t) { load(d_t, decltype(d_t)::value); });
+  for (int s0 = 0; s0 < nsteps; s0 += D) {
+    // slot d holds step s0 + d; once it is used, it takes step s0 + d + D
+    static_for<D>([&](auto d_t) {
+      constexpr int d = decltype(d_t)::value;
+      if (s0 + d < nsteps) consume(d_t);
+      load(d_t, s0 + d + D);
+    });
+  }
+
+  if (m >= rows) return;
+  if constexpr (SWIGLU) {
+    // outputs o0 + 2 CPL g + CPL v + c (v = 0, 1): gate in element v, up in
+    // element v + 2; 8-output chunks
+    const int o = kOut * p + 2 * CPL * g;
+#pragma unroll
+    for (int u = 0; u < CPL / 4; ++u) {
+      if (o + 8 * u < N) {
+        float hv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int v = (8 * u + i) / CPL, c = (8 * u + i) % CPL;
+          const float gt = acc[c][v];
+          hv[i] = gt / (1.f + __expf(-gt)) * acc[c][v + 2];
+        }
+        *reinterpret_cast<u32x4*>(C + int64_t(r0 + m) * ldc + o + 8 * u) =
+            u32x4{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]), pack_bf16x2(hv[4], hv[5]),
+                  pack_bf16x2(hv[6], hv[7])};
+      }
+    }
+  } else {
+    // columns c0 + 4 CPL g + CPL v + c; 8-column chunks
+    int dst = -1;
+    float wt = 0.f;
+    if constexpr (FUSE) {
+      const int2 ri = row_info[r0 + m];
+      dst = ri.x;
+      wt = __int_as_float(ri.y);
+    }
+    uint16_t* const base = dst >= 0 ? y + int64_t(dst) * ldc : C + int64_t(r0 + m) * ldc;
+    const int c0 = kOut * p + 4 * CPL * g;
+#pragma unroll
+    for (int u = 0; u < CPL / 2; ++u) {
+      if (c0 + 8 * u < N) {
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = 8 * u + 2 * i;  // column pair (j, j + 1) of the lane's 4 CPL
+          uint32_t lo = f32_to_bf16_bits(acc[j % CPL][j / CPL]);
+          uint32_t hi = f32_to_bf16_bits(acc[(j + 1) % CPL][(j + 1) / CPL]);
+          if (FUSE && dst >= 0) {
+            lo = f32_to_bf16_bits(fmaf(wt, bf16_to_f32(uint16_t(lo)), -0.f));
+            hi = f32_to_bf16_bits(fmaf(wt, bf16_to_f32(uint16_t(hi)), -0.f));
+          }
+          o[i] = lo | (hi << 16);
+        }
+        *reinterpret_cast<u32x4*>(base + c0 + 8 * u) = u32x4{o[0], o[1], o[2], o[3]};
+      }
+    }
+  }
+}
+
+template <bool SWIGLU, bool FUSE>
+hipError_t launch(const uint16_t* A, int lda, const int32_t* gather_src, int gather_k, int gather_rows,
+                  const int32_t* offsets, int E_local, int64_t capacity, const uint16_t* W, int64_t w_expert_stride,
+                  int ldw, int K, int N, int up_off, uint16_t* C, int ldc, const int2* row_info, uint16_t* y,
+                  hipStream_t stream) {
+  constexpr int D = 4;
+  constexpr int CPL = 8;
+  constexpr int WAUX = 2;
+  const int64_t npanel = ceil_div(N, SWIGLU ? 8 * CPL : 16 * CPL);
+  const int64_t waves = npanel * E_local;
+  hipLaunchKernelGGL((grouped_gemv_kernel<SWIGLU, FUSE, D, CPL, WAUX>), dim3(unsigned(ceil_div(waves, kWaves))),
+                     dim3(kThreads), 0, stream, A, lda, gather_src, gather_k, gather_rows, offsets, E_local,
+                     capacity, W, w_expert_stride, ldw, K, N, up_off, C, ldc, row_info, y);
+  return hipGetLastError();
+}
+
+}  // namespace gemv
+
+bool grouped_gemv_usable(int64_t capacity, int E_local, int K) {
+  // about 64 rows per local expert or fewer on average; K in whole steps
+  return K % gemv::kStepK == 0 && capacity <= 64 * int64_t(E_local);
+}
+
+int grouped_gemv_max_rows() { return gemv::kMaxRows; }
+
+hipError_t launch_grouped_gemv1(const uint16_t* A, int lda, const int32_t* gather_src, int gather_k, int gather_rows,
+                                const int32_t* offsets, int E_local, int64_t capacity, const uint16_t* w_gate_up,
+                                int H, int I, uint16_t* h, hipStream_t stream) {
+  return gemv::launch<true, false>(A, lda, gather_src, gather_k, gather_rows, offsets, E_local, capacity, w_gate_up,
+                                   int64_t(H) * 2 * I, 2 * I, H, I, I, h, I, nullptr, nullptr, stream);
+}
+
+hipError_t launch_grouped_gemv2(const uint16_t* h, const int32_t* offsets, int E_local, int64_t capacity,
+                                const uint16_t* w_down, int H, int I, const int2* row_info, uint16_t* out,
+                                uint16_t* y, hipStream_t stream) {
+  if (row_info != nullptr)
+    return gemv::launch<false, true>(h, I, nullptr, 1, 0, offsets, E_local, capacity, w_down, int64_t(I) * H, H, I, H,
+                                     0, out, H, row_info, y, stream);
+  return gemv::launch<false, false>(h, I, nullptr, 1, 0, offsets, E_local, capacity, w_down, int64_t(I) * H, H, I, H,
+                                    0, out, H, nullptr, nullptr, stream);
+}
+
+}  // namespace moe

@@ -57,6 +57,24 @@ hipError_t launch_expert_gemm2_fused(const uint16_t* h, const int32_t* offsets, 
                                      int E_local, int64_t capacity, const int2* row_info, uint16_t* out, uint16_t* y,
                                      hipStream_t stream);
 
+// Grouped GEMV for experts with few rows (at most grouped_gemv_max_rows()):
+// each wave streams one weight panel of one expert; experts with more rows
+// are skipped (the tile kernel runs them). Usable when K (H for the gate/up
+// GEMM, I for the down GEMM) is a multiple of 32; chosen when the capacity
+// averages at most 64 rows per local expert.
+bool grouped_gemv_usable(int64_t capacity, int E_local, int K);
+int grouped_gemv_max_rows();
+// gate/up + SwiGLU: rows from A [.., H] (row n of a segment is row
+// gather_src[n] / gather_k of A when gather_src is given) into h [capacity, I]
+hipError_t launch_grouped_gemv1(const uint16_t* A, int lda, const int32_t* gather_src, int gather_k, int gather_rows,
+                                const int32_t* offsets, int E_local, int64_t capacity, const uint16_t* w_gate_up,
+                                int H, int I, uint16_t* h, hipStream_t stream);
+// down: h [capacity, I] into out [capacity, H]; with row_info, rows of
+// single-selection tokens go to y as launch_expert_gemm2_fused writes them
+hipError_t launch_grouped_gemv2(const uint16_t* h, const int32_t* offsets, int E_local, int64_t capacity,
+                                const uint16_t* w_down, int H, int I, const int2* row_info, uint16_t* out,
+                                uint16_t* y, hipStream_t stream);
+
 // row_info of launch_expert_gemm2_fused from inv and topk_w (one thread per
 // token); rows of tokens with two or more local selections get {-1, 0}.
 hipError_t launch_single_rows(const int32_t* inv, const float* topk_w, int T, int k, int2* row_info,

@@ -1,0 +1,51 @@
+"""The grouped GEMV (experts with at most 16 rows) against the tile kernel.
+
+moe_expert_ffn picks the GEMV when its capacity averages at most 64 rows per
+local expert, so the same rows run through both kernels by passing them once
+in a buffer of exactly their size and once padded to more than 64 rows per
+expert (rows past offsets[E_local] are never read). Every output element is
+one MFMA chain over k in the same order in both kernels, so h and the expert
+outputs must agree bit for bit. Inputs are drawn on the GPU; this compares
+two paths of the library, the oracle comparisons of the same kernels are in
+test_gpu_parity.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import expert_token_routing_amd as M
+from tests.gpu_helpers import device, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("H,I,counts", [
+    (224, 160, [0, 1, 5, 16, 17, 3, 40, 16]),   # 7 / 5 k-steps, ragged 64-column panels, both kernels
+    (256, 96, [16, 16, 16, 16]),                # exactly 16 rows everywhere
+    (64, 64, [2, 0, 16]),                       # 2 k-steps, one panel
+    (1024, 512, [9, 12, 1, 30, 0, 16, 7, 11]),  # several ring turns
+    (7168, 2048, [14, 9, 0, 16, 1, 33, 8, 12]), # the DeepSeek-R1 expert shape
+], ids=["ragged", "full16", "tiny", "mid", "dsr1"])
+def test_grouped_gemv_matches_tiles(H, I, counts):
+    dev = device()
+    E_local = len(counts)
+    N = int(sum(counts))
+    cap_big = 64 * E_local + 1
+    assert N <= 64 * E_local
+    g = torch.Generator(device=dev).manual_seed(11)
+    x = (torch.randn((cap_big, H), generator=g, device=dev) / H ** 0.5).to(torch.bfloat16)
+    wgu = (torch.randn((E_local, H, 2 * I), generator=g, device=dev) / H ** 0.5).to(torch.bfloat16)
+    wd = (torch.randn((E_local, I, H), generator=g, device=dev) / I ** 0.5).to(torch.bfloat16)
+    offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=dev)
+    say(f"grouped GEMV H={H} I={I} counts={counts}")
+    h1, o1 = M.moe_expert_ffn(x[:max(N, 1)].contiguous(), offsets, wgu, wd)
+    say(f"tiles H={H} I={I} capacity={cap_big}")
+    h2, o2 = M.moe_expert_ffn(x, offsets, wgu, wd)
+    torch.cuda.synchronize()
+    hb1, hb2 = h1[:N].view(torch.int16), h2[:N].view(torch.int16)
+    ob1, ob2 = o1[:N].view(torch.int16), o2[:N].view(torch.int16)
+    assert torch.equal(hb1, hb2), int((hb1 != hb2).sum())
+    assert torch.equal(ob1, ob2), int((ob1 != ob2).sum())
+    assert torch.isfinite(o1[:N].float()).all()
