@@ -405,15 +405,12 @@ __device__ __forceinline__ void run_tile(MOE_LDS char* lds, const uint16_t* __re
 // FUSE (down GEMM): row_info[n] = {token, combine weight bits} for row n of a
 // token with exactly one local selection, {-1, 0} otherwise; those rows are
 // written to y [T, ldc] instead of C.
-// Experts with at most skip_rows rows get no tiles (the grouped GEMV runs
-// them).
 template <bool SWIGLU, bool FUSE, bool HALF>
 __global__ void __launch_bounds__(dma::kThreads)
 panel_gemm_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __restrict__ offsets, int E_local,
                   int64_t capacity, const uint16_t* __restrict__ W, int64_t w_expert_stride, int ldw,
                   uint16_t* __restrict__ C, int ldc, int K, int N, int up_off, const int32_t* __restrict__ gather_src,
-                  int gather_k, int gather_rows, const int2* __restrict__ row_info, uint16_t* __restrict__ y,
-                  int skip_rows) {
+                  int gather_k, int gather_rows, const int2* __restrict__ row_info, uint16_t* __restrict__ y) {
   using namespace dma::panel;
   static_assert(!(FUSE && SWIGLU), "the combine is fused into the down GEMM only");
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
@@ -440,7 +437,7 @@ panel_gemm_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __rest
       const int64_t a = min<int64_t>(max<int64_t>(offsets[i], 0), capacity);
       const int64_t b = max<int64_t>(a, min<int64_t>(offsets[i + 1], capacity));
       s_off[i] = int(a);
-      me[q] = b - a > skip_rows ? int(b - a) : 0;
+      me[q] = int(b - a);
       if (i == E_local - 1) s_off[E_local] = int(b);
     }
   }
@@ -595,34 +592,27 @@ template <bool SWIGLU, bool FUSE>
 hipError_t launch_panel(int64_t tiles, hipStream_t stream, const uint16_t* A, int lda, const int32_t* offsets,
                         int E_local, int64_t capacity, const uint16_t* W, int64_t w_expert_stride, int ldw,
                         uint16_t* C, int ldc, int K, int N, int up_off, const int32_t* gather_src, int gather_k,
-                        int gather_rows, const int2* row_info, uint16_t* y) {
-  // With few rows per expert on average, the experts with at most
-  // grouped_gemv_max_rows() rows go to the grouped GEMV and the tiles take
-  // the rest (none can have more when the capacity is that small).
-  int skip_rows = 0;
-  if (grouped_gemv_usable(capacity, E_local, K)) {
-    const hipError_t err =
-        SWIGLU ? launch_grouped_gemv1(A, lda, gather_src, gather_k, gather_rows, offsets, E_local, capacity, W, K,
-                                      N, C, stream)
-               : launch_grouped_gemv2(A, offsets, E_local, capacity, W, N, K, row_info, C, y, stream);
-    if (err != hipSuccess) return err;
-    skip_rows = grouped_gemv_max_rows();
-    if (capacity <= skip_rows) return hipSuccess;
-  }
+                        int gather_rows, const int2* row_info, uint16_t* y, int64_t rows_hint) {
+  // With few rows per expert expected, the grouped GEMV takes every expert.
+  if (grouped_gemv_usable(rows_hint, K))
+    return SWIGLU ? launch_grouped_gemv1(A, lda, gather_src, gather_k, gather_rows, offsets, E_local, capacity, W, K,
+                                         N, C, stream)
+                  : launch_grouped_gemv2(A, offsets, E_local, capacity, W, N, K, row_info, C, y, stream);
   const bool half = K % dma::panel::kSK != 0;
   auto* kern = half ? panel_gemm_kernel<SWIGLU, FUSE, true> : panel_gemm_kernel<SWIGLU, FUSE, false>;
   hipLaunchKernelGGL(kern, dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream, A, lda, offsets, E_local, capacity,
-                     W, w_expert_stride, ldw, C, ldc, K, N, up_off, gather_src, gather_k, gather_rows, row_info, y,
-                     skip_rows);
+                     W, w_expert_stride, ldw, C, ldc, K, N, up_off, gather_src, gather_k, gather_rows, row_info, y);
   return hipGetLastError();
 }
 
 hipError_t launch_expert_gemm1(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_gate_up, int H,
-                               int I, int E_local, int64_t capacity, uint16_t* h, hipStream_t stream) {
+                               int I, int E_local, int64_t capacity, uint16_t* h, hipStream_t stream,
+                               int64_t rows_hint) {
   if (H % dma::kBK == 0) {
     const int64_t tiles = (ceil_div(capacity, kRowCapMin) + E_local) * ceil_div(I, dma::panel::kBN / 2);
     return launch_panel<true, false>(tiles, stream, x_perm, H, offsets, E_local, capacity, w_gate_up,
-                                     int64_t(H) * 2 * I, 2 * I, h, I, H, I, I, nullptr, 1, 0, nullptr, nullptr);
+                                     int64_t(H) * 2 * I, 2 * I, h, I, H, I, I, nullptr, 1, 0, nullptr, nullptr,
+                                     rows_hint);
   }
   const int64_t mt_bound = ceil_div(capacity, kFfnBM) + E_local;
   const unsigned grid = persistent_grid(mt_bound * ceil_div(I, 128));
@@ -632,11 +622,11 @@ hipError_t launch_expert_gemm1(const uint16_t* x_perm, const int32_t* offsets, c
 }
 
 hipError_t launch_expert_gemm2(const uint16_t* h, const int32_t* offsets, const uint16_t* w_down, int H, int I,
-                               int E_local, int64_t capacity, uint16_t* out, hipStream_t stream) {
+                               int E_local, int64_t capacity, uint16_t* out, hipStream_t stream, int64_t rows_hint) {
   if (I % dma::kBK == 0) {
     const int64_t tiles = (ceil_div(capacity, kRowCapMin) + E_local) * ceil_div(H, dma::panel::kBN);
     return launch_panel<false, false>(tiles, stream, h, I, offsets, E_local, capacity, w_down, int64_t(I) * H, H,
-                                      out, H, I, H, 0, nullptr, 1, 0, nullptr, nullptr);
+                                      out, H, I, H, 0, nullptr, 1, 0, nullptr, nullptr, rows_hint);
   }
   const int64_t mt_bound = ceil_div(capacity, kFfnBM) + E_local;
   const unsigned grid = persistent_grid(mt_bound * ceil_div(H, 256));
@@ -649,28 +639,31 @@ bool expert_gemm2_can_fuse(int I) { return I % dma::kBK == 0; }
 
 hipError_t launch_expert_gemm2_fused(const uint16_t* h, const int32_t* offsets, const uint16_t* w_down, int H, int I,
                                      int E_local, int64_t capacity, const int2* row_info, uint16_t* out, uint16_t* y,
-                                     hipStream_t stream) {
+                                     hipStream_t stream, int64_t rows_hint) {
   const int64_t tiles = (ceil_div(capacity, kRowCapMin) + E_local) * ceil_div(H, dma::panel::kBN);
   return launch_panel<false, true>(tiles, stream, h, I, offsets, E_local, capacity, w_down, int64_t(I) * H, H, out,
-                                   H, I, H, 0, nullptr, 1, 0, row_info, y);
+                                   H, I, H, 0, nullptr, 1, 0, row_info, y, rows_hint);
 }
 
 bool expert_gemm1_can_gather(int T, int H) { return H % dma::kBK == 0 && int64_t(T) * H * 2 < (int64_t(1) << 31); }
 
 hipError_t launch_expert_gemm1_gather(const uint16_t* x, const int32_t* perm_src, int T, int k, const int32_t* offsets,
                                       const uint16_t* w_gate_up, int H, int I, int E_local, int64_t capacity,
-                                      uint16_t* h, hipStream_t stream) {
+                                      uint16_t* h, hipStream_t stream, int64_t rows_hint) {
   const int64_t tiles = (ceil_div(capacity, kRowCapMin) + E_local) * ceil_div(I, dma::panel::kBN / 2);
   return launch_panel<true, false>(tiles, stream, x, H, offsets, E_local, capacity, w_gate_up, int64_t(H) * 2 * I,
-                                   2 * I, h, I, H, I, I, perm_src, k, T, nullptr, nullptr);
+                                   2 * I, h, I, H, I, I, perm_src, k, T, nullptr, nullptr, rows_hint);
 }
 
 hipError_t launch_expert_ffn(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_gate_up,
                              const uint16_t* w_down, int H, int I, int E_local, int64_t capacity, uint16_t* h,
                              uint16_t* out, hipStream_t stream) {
-  hipError_t err = launch_expert_gemm1(x_perm, offsets, w_gate_up, H, I, E_local, capacity, h, stream);
+  // without the routing, the capacity spread over the local experts is the
+  // expected row count
+  const int64_t rows_hint = ceil_div(capacity, E_local);
+  hipError_t err = launch_expert_gemm1(x_perm, offsets, w_gate_up, H, I, E_local, capacity, h, stream, rows_hint);
   if (err != hipSuccess) return err;
-  return launch_expert_gemm2(h, offsets, w_down, H, I, E_local, capacity, out, stream);
+  return launch_expert_gemm2(h, offsets, w_down, H, I, E_local, capacity, out, stream, rows_hint);
 }
 
 }  // namespace moe

@@ -242,6 +242,9 @@ static int forward_impl(const moe_bf16* x, const float* w_router, const float* b
   // GEMM1 reads the token vectors in place when it can, so dispatch only
   // builds the tables; otherwise the rows are copied out first.
   const bool gather = expert_gemm1_can_gather(T, H);
+  // rows a local expert holds when the T k selections spread evenly over
+  // the E experts (the GEMMs take the grouped GEMV when that is small)
+  const int64_t rows_hint = ceil_div(int64_t(T) * k, E);
   if (err == hipSuccess)
     err = gather ? launch_dispatch_index(topk_idx, T, E, k, e0, E_local, counts, offsets, perm_src, inv, chunks, stream)
                  : launch_dispatch(x, topk_idx, T, H, E, k, e0, E_local, counts, offsets, perm_src, inv, x_perm,
@@ -249,13 +252,14 @@ static int forward_impl(const moe_bf16* x, const float* w_router, const float* b
   if (err == hipSuccess && fuse) err = launch_single_rows(inv, topk_w, T, k, row_info, stream);
   if (err == hipSuccess) err = mark(2);
   if (err == hipSuccess)
-    err = gather ? launch_expert_gemm1_gather(x, perm_src, T, k, offsets, w_gate_up, H, I, E_local, cap, h, stream)
-                 : launch_expert_gemm1(x_perm, offsets, w_gate_up, H, I, E_local, cap, h, stream);
+    err = gather ? launch_expert_gemm1_gather(x, perm_src, T, k, offsets, w_gate_up, H, I, E_local, cap, h, stream,
+                                              rows_hint)
+                 : launch_expert_gemm1(x_perm, offsets, w_gate_up, H, I, E_local, cap, h, stream, rows_hint);
   if (err == hipSuccess) err = mark(3);
   if (err == hipSuccess)
     err = fuse ? launch_expert_gemm2_fused(h, offsets, w_down, H, I, E_local, cap, row_info, out,
-                                           static_cast<uint16_t*>(y), stream)
-               : launch_expert_gemm2(h, offsets, w_down, H, I, E_local, cap, out, stream);
+                                           static_cast<uint16_t*>(y), stream, rows_hint)
+               : launch_expert_gemm2(h, offsets, w_down, H, I, E_local, cap, out, stream, rows_hint);
   if (err == hipSuccess) err = mark(4);
   if (err == hipSuccess) err = launch_combine(out, inv, topk_w, T, H, k, y, y_f32, stream, fuse);
   if (err == hipSuccess) err = mark(5);

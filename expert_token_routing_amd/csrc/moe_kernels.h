@@ -34,10 +34,13 @@ hipError_t launch_expert_ffn(const uint16_t* x_perm, const int32_t* offsets, con
                              uint16_t* out, hipStream_t stream);
 
 // The two grouped GEMMs on their own (what launch_expert_ffn runs in order).
+// rows_hint: the rows a local expert is expected to hold; at most 16
+// selects the grouped GEMV (any routing gives correct results either way).
 hipError_t launch_expert_gemm1(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_gate_up, int H,
-                               int I, int E_local, int64_t capacity, uint16_t* h, hipStream_t stream);
+                               int I, int E_local, int64_t capacity, uint16_t* h, hipStream_t stream,
+                               int64_t rows_hint);
 hipError_t launch_expert_gemm2(const uint16_t* h, const int32_t* offsets, const uint16_t* w_down, int H, int I,
-                               int E_local, int64_t capacity, uint16_t* out, hipStream_t stream);
+                               int E_local, int64_t capacity, uint16_t* out, hipStream_t stream, int64_t rows_hint);
 
 // GEMM1 reading the token vectors of x in place (row n of a segment is token
 // perm_src[n] / k) instead of a dispatched copy; usable when
@@ -45,7 +48,7 @@ hipError_t launch_expert_gemm2(const uint16_t* h, const int32_t* offsets, const 
 bool expert_gemm1_can_gather(int T, int H);
 hipError_t launch_expert_gemm1_gather(const uint16_t* x, const int32_t* perm_src, int T, int k, const int32_t* offsets,
                                       const uint16_t* w_gate_up, int H, int I, int E_local, int64_t capacity,
-                                      uint16_t* h, hipStream_t stream);
+                                      uint16_t* h, hipStream_t stream, int64_t rows_hint);
 
 // Down GEMM with the combine of single-selection tokens in its epilogue:
 // row_info[n] = {token, bits of its combine weight} when row n's token has
@@ -55,15 +58,14 @@ hipError_t launch_expert_gemm1_gather(const uint16_t* x, const int32_t* perm_src
 bool expert_gemm2_can_fuse(int I);
 hipError_t launch_expert_gemm2_fused(const uint16_t* h, const int32_t* offsets, const uint16_t* w_down, int H, int I,
                                      int E_local, int64_t capacity, const int2* row_info, uint16_t* out, uint16_t* y,
-                                     hipStream_t stream);
+                                     hipStream_t stream, int64_t rows_hint);
 
-// Grouped GEMV for experts with few rows (at most grouped_gemv_max_rows()):
-// each wave streams one weight panel of one expert; experts with more rows
-// are skipped (the tile kernel runs them). Usable when K (H for the gate/up
-// GEMM, I for the down GEMM) is a multiple of 32; chosen when the capacity
-// averages at most 64 rows per local expert.
-bool grouped_gemv_usable(int64_t capacity, int E_local, int K);
-int grouped_gemv_max_rows();
+// Grouped GEMV for few rows per expert: each wave streams one weight panel
+// of one expert for up to 32 of its rows (an expert with more gets more
+// waves). Usable when K (H for the gate/up GEMM, I for the down GEMM) is a
+// multiple of 32; chosen when the expected rows per local expert
+// (rows_hint) are at most 16.
+bool grouped_gemv_usable(int64_t rows_hint, int K);
 // gate/up + SwiGLU: rows from A [.., H] (row n of a segment is row
 // gather_src[n] / gather_k of A when gather_src is given) into h [capacity, I]
 hipError_t launch_grouped_gemv1(const uint16_t* A, int lda, const int32_t* gather_src, int gather_k, int gather_rows,

@@ -1,6 +1,6 @@
-"""The grouped GEMV (experts with at most 16 rows) against the tile kernel.
+"""The grouped GEMV (experts with at most 32 rows) against the tile kernel.
 
-moe_expert_ffn picks the GEMV when its capacity averages at most 64 rows per
+moe_expert_ffn picks the GEMV when its capacity averages at most 16 rows per
 local expert, so the same rows run through both kernels by passing them once
 in a buffer of exactly their size and once padded to more than 64 rows per
 expert (rows past offsets[E_local] are never read). Every output element is
@@ -23,17 +23,20 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("H,I,counts", [
     (224, 160, [0, 1, 5, 16, 17, 3, 40, 16]),   # 7 / 5 k-steps, ragged 64-column panels, both kernels
-    (256, 96, [16, 16, 16, 16]),                # exactly 16 rows everywhere
+    (256, 96, [16, 16, 16, 16]),                # exactly 16 rows everywhere (one row group)
+    (256, 96, [32, 31, 17, 16, 0, 0]),          # two row groups, full and ragged
+    (256, 96, [100, 3, 0, 5, 7, 1, 0, 2]),      # a hot expert: four 32-row waves per panel
     (64, 64, [2, 0, 16]),                       # 2 k-steps, one panel
+    (32, 32, [16, 3, 0, 1]),                    # one k-step: every later ring slot reloads it
     (1024, 512, [9, 12, 1, 30, 0, 16, 7, 11]),  # several ring turns
     (7168, 2048, [14, 9, 0, 16, 1, 33, 8, 12]), # the DeepSeek-R1 expert shape
-], ids=["ragged", "full16", "tiny", "mid", "dsr1"])
+], ids=["ragged", "full16", "two_groups", "hot", "tiny", "one_step", "mid", "dsr1"])
 def test_grouped_gemv_matches_tiles(H, I, counts):
     dev = device()
     E_local = len(counts)
     N = int(sum(counts))
     cap_big = 64 * E_local + 1
-    assert N <= 64 * E_local
+    assert N <= 16 * E_local
     g = torch.Generator(device=dev).manual_seed(11)
     x = (torch.randn((cap_big, H), generator=g, device=dev) / H ** 0.5).to(torch.bfloat16)
     wgu = (torch.randn((E_local, H, 2 * I), generator=g, device=dev) / H ** 0.5).to(torch.bfloat16)

@@ -54,12 +54,14 @@ SMALL_CASES = [
     ragged("dma_ragged_n", T=300, H=192, I=320, E=12, k=3, e0=4, E_local=5),
     ragged("dma_multi_mtile", T=1500, H=256, I=384, E=4, k=2, e0=0, E_local=4),
     ragged("dma_wide_n", T=640, H=576, I=448, E=16, k=4, e0=3, E_local=6, renormalize=0),
-    # few rows per expert (capacity <= 64 per local expert): the grouped GEMV
-    # takes the experts with up to 16 rows, the tiles the rest; 7 and 5
-    # k-steps (fewer than its ring of loads), half a 64-column panel at the
-    # end of H; then H off the 32 grid (gate/up on the fallback GEMM, down on
-    # the GEMV with an 8-column tail)
-    ragged("gemv_ragged", T=150, H=224, I=160, E=24, k=4, e0=5, E_local=10),
+    # few rows per expert (T k / E <= 16): the forward's GEMMs take the
+    # grouped GEMV; 7 and 5 k-steps (fewer than its ring of loads), ragged
+    # 128-column panels at the end of H, experts of one and two 16-row groups;
+    # then a skewed router whose hottest local expert needs several 32-row
+    # waves per panel; then H off the 32 grid (gate/up on the fallback GEMM,
+    # down on the GEMV with an 8-column tail)
+    ragged("gemv_ragged", T=120, H=224, I=160, E=40, k=5, e0=5, E_local=12),
+    ragged("gemv_hot", T=120, H=224, I=160, E=40, k=5, e0=5, E_local=12, zipf_s=1.0),
     ragged("gemv_mixed", T=40, H=200, I=96, E=6, k=2, e0=1, E_local=4),
     # k extents that end in half a 64-deep stage (H % 64 == I % 64 == 32)
     ragged("dma_half_stage", T=700, H=160, I=224, E=8, k=2, e0=2, E_local=4),
