@@ -345,13 +345,12 @@ hipError_t launch(const uint16_t* A, int lda, const int32_t* gather_src, int gat
 
 }  // namespace gemv
 
-bool grouped_gemv_usable(int64_t rows_hint, int K) {
-  // At most 16 rows per local expert expected, so that nearly every expert
-  // fits one wave of 32 rows: waves of different row groups reading the same
-  // panel share its lines badly (measured: with a third of the experts above
-  // 32 rows the gate/up GEMM ran slower than the tile kernel). K in whole
-  // steps.
-  return K % gemv::kStepK == 0 && rows_hint <= gemv::kGroupRows / 2;
+bool grouped_gemv_usable(int64_t rows_hint, int K, bool gate_up) {
+  // Measured against the tile kernel on DeepSeek-R1-shaped shares: the
+  // gate/up GEMM wins up to 16 expected rows per local expert (nearly every
+  // expert fits one wave of 32 rows; at 24 and 32 it lost), the down GEMM up
+  // to 32. K in whole steps.
+  return K % gemv::kStepK == 0 && rows_hint <= (gate_up ? gemv::kGroupRows / 2 : gemv::kGroupRows);
 }
 
 hipError_t launch_grouped_gemv1(const uint16_t* A, int lda, const int32_t* gather_src, int gather_k, int gather_rows,

@@ -34,8 +34,8 @@ hipError_t launch_expert_ffn(const uint16_t* x_perm, const int32_t* offsets, con
                              uint16_t* out, hipStream_t stream);
 
 // The two grouped GEMMs on their own (what launch_expert_ffn runs in order).
-// rows_hint: the rows a local expert is expected to hold; at most 16
-// selects the grouped GEMV (any routing gives correct results either way).
+// rows_hint: the rows a local expert is expected to hold; few select the
+// grouped GEMV (any routing gives correct results either way).
 hipError_t launch_expert_gemm1(const uint16_t* x_perm, const int32_t* offsets, const uint16_t* w_gate_up, int H,
                                int I, int E_local, int64_t capacity, uint16_t* h, hipStream_t stream,
                                int64_t rows_hint);
@@ -64,8 +64,8 @@ hipError_t launch_expert_gemm2_fused(const uint16_t* h, const int32_t* offsets, 
 // of one expert for up to 32 of its rows (an expert with more gets more
 // waves). Usable when K (H for the gate/up GEMM, I for the down GEMM) is a
 // multiple of 32; chosen when the expected rows per local expert
-// (rows_hint) are at most 16.
-bool grouped_gemv_usable(int64_t rows_hint, int K);
+// (rows_hint) are at most 16 (gate/up GEMM) or 32 (down GEMM).
+bool grouped_gemv_usable(int64_t rows_hint, int K, bool gate_up);
 // gate/up + SwiGLU: rows from A [.., H] (row n of a segment is row
 // gather_src[n] / gather_k of A when gather_src is given) into h [capacity, I]
 hipError_t launch_grouped_gemv1(const uint16_t* A, int lda, const int32_t* gather_src, int gather_k, int gather_rows,
