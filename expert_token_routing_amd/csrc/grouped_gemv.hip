@@ -15,13 +15,15 @@
 // Wave geometry. A wave owns one panel of 16 CPL weight columns of one expert
 // (CPL = 4 or 8 columns per lane) and walks k in steps of 32. Lane l = 16 g + m
 // loads, per step, CPL columns (2 CPL bytes) from each of the 8 weight rows
-// k0 + 8 g .. k0 + 8 g + 7, and the 16 bytes of token row m at the same 8 k.
+// k0 + 8 g .. k0 + 8 g + 7, and the 16 bytes of token row m of each 16-row
+// group at the same 8 k.
 // Transposing its 8 x CPL block in registers gives the lane, for each of its
 // columns c, the 8 k-values that lane (g, m) of a v_mfma_f32_16x16x32_bf16 A
 // operand holds for A row m. So MFMA c multiplies the 16 columns
-// colbase(m) + c (A rows m = 0..15) by the token rows (B columns m), and CPL
-// MFMAs per step cover the panel. Afterwards lane (g, m) holds, in
-// accumulator c, element v, column colbase(4 g + v) + c of token row m.
+// colbase(m) + c (A rows m = 0..15) by a group's token rows (B columns m),
+// and CPL MFMAs per step and group cover the panel. Afterwards lane (g, m)
+// holds, in accumulator c of a group, element v, column colbase(4 g + v) + c
+// of the group's token row m.
 //
 // Panel columns. Down GEMM: the panel is 16 CPL consecutive output columns,
 // colbase(m) = CPL m, so a lane ends with the 4 CPL consecutive columns
