@@ -63,6 +63,8 @@ SMALL_CASES = [
     ragged("gemv_ragged", T=120, H=224, I=160, E=40, k=5, e0=5, E_local=12),
     ragged("gemv_hot", T=120, H=224, I=160, E=40, k=5, e0=5, E_local=12, zipf_s=1.0),
     ragged("gemv_mixed", T=40, H=200, I=96, E=6, k=2, e0=1, E_local=4),
+    # the GEMV's wave table at its limit: 1024 local experts, most without rows
+    ragged("gemv_1024_experts", T=100, H=64, I=64, E=1024, k=4, e0=0, E_local=1024),
     # k extents that end in half a 64-deep stage (H % 64 == I % 64 == 32)
     ragged("dma_half_stage", T=700, H=160, I=224, E=8, k=2, e0=2, E_local=4),
     # few tokens for a long hidden dimension: the router's k range in 4 parts
