@@ -338,7 +338,9 @@ dispatch_place_copy_kernel(const uint16_t* __restrict__ x, const int32_t* __rest
   }
   const uint64_t dests = ballot(d >= 0);
   if (dests == 0) return;
-  constexpr int U = 4;
+  // 16 vectors per lane in flight (measured: 4 -> 16 took moe_dispatch from
+  // about 70.0 to 69.4 us at the DeepSeek-R1 share)
+  constexpr int U = 16;
   const int nv = H / 8;
   const u32x4* src = reinterpret_cast<const u32x4*>(x + int64_t(t) * H);
   for (int v0 = 0; v0 < nv; v0 += 64 * U) {
