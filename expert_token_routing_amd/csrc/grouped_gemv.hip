@@ -50,8 +50,6 @@ namespace gemv {
 using dma::panel::f32x4v;
 using dma::panel::mfma16x16x32;
 
-constexpr int kWaves = 4;             // waves per workgroup (independent)
-constexpr int kThreads = 64 * kWaves;
 constexpr int kStepK = 32;            // k per step
 constexpr int kGroupRows = 32;        // token rows of one wave (two groups of 16)
 constexpr int kMaxLocal = 1024;       // local experts (the limit on E)
@@ -251,10 +249,10 @@ __device__ __forceinline__ void gemv_panel(const GemvArgs& a, int p, int rows, i
 // lines through L2 (those use plain loads). Every workgroup builds the prefix of waves per expert
 // from the offsets; the grid covers the most waves any routing can need,
 // (ceil(capacity / 32) + E_local) x panels, and waves past the total exit.
-// At most 256 registers per lane (accumulators included), so that two waves
-// share a SIMD.
-template <bool SWIGLU, bool FUSE, int CPL, int WAUX>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+// NW waves per workgroup (independent but for the table). At most 256
+// registers per lane (accumulators included), so that two waves share a SIMD.
+template <bool SWIGLU, bool FUSE, int CPL, int WAUX, int NW>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 grouped_gemv_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __restrict__ gather_src, int gather_k,
                     int gather_rows, const int32_t* __restrict__ offsets, int E_local, int64_t capacity,
                     const uint16_t* __restrict__ W, int64_t w_expert_stride, int ldw, int K, int N, int up_off,
@@ -262,10 +260,11 @@ grouped_gemv_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __re
   static_assert(!(FUSE && SWIGLU), "the combine is fused into the down GEMM only");
   static_assert(CPL == 4 || CPL == 8, "4 or 8 columns per lane");
   constexpr int kOut = SWIGLU ? 8 * CPL : 16 * CPL;  // outputs per panel
+  constexpr int kThreads = 64 * NW;
   constexpr int kPerT = kMaxLocal / kThreads;
   __shared__ int s_off[kMaxLocal + 1];   // segment bounds, clamped into [0, capacity]
   __shared__ int s_wpre[kMaxLocal + 1];  // first wave of each expert
-  __shared__ int s_tmp[kWaves];
+  __shared__ int s_tmp[NW];
   const int npanel = (N + kOut - 1) / kOut;
   int nw[kPerT];
   int sum = 0;
@@ -291,7 +290,7 @@ grouped_gemv_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __re
     pre += nw[q];
   }
   __syncthreads();
-  const int wave = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * kWaves + int(threadIdx.x >> 6));
+  const int wave = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * NW + int(threadIdx.x >> 6));
   if (wave >= total) return;
   // the expert: the last one whose first wave is at or before this one
   // (experts without rows own no waves)
@@ -339,9 +338,21 @@ hipError_t launch(const uint16_t* A, int lda, const int32_t* gather_src, int gat
   constexpr int WAUX = 2;
   const int64_t npanel = ceil_div(N, SWIGLU ? 8 * CPL : 16 * CPL);
   const int64_t waves = (ceil_div(capacity, kGroupRows) + E_local) * npanel;
-  hipLaunchKernelGGL((grouped_gemv_kernel<SWIGLU, FUSE, CPL, WAUX>), dim3(unsigned(ceil_div(waves, kWaves))),
-                     dim3(kThreads), 0, stream, A, lda, gather_src, gather_k, gather_rows, offsets, E_local,
-                     capacity, W, w_expert_stride, ldw, K, N, up_off, C, ldc, row_info, y);
+  // Four waves per workgroup (neighbouring panels on one CU) when there are
+  // panels enough to fill the chip; with few (few local experts, narrow
+  // outputs) one, so that the waves spread over as many CUs as possible.
+  // Measured: the DeepSeek-R1 decode step's 1024 / 1792 waves run 279 / 148 us
+  // in fours and 339 / 162 us alone; a GPT-OSS-20B decode step's down GEMM
+  // (4 experts x 23 panels) 86 us in fours and 34 us alone.
+  if (E_local * npanel >= 512) {
+    hipLaunchKernelGGL((grouped_gemv_kernel<SWIGLU, FUSE, CPL, WAUX, 4>), dim3(unsigned(ceil_div(waves, 4))),
+                       dim3(256), 0, stream, A, lda, gather_src, gather_k, gather_rows, offsets, E_local, capacity, W,
+                       w_expert_stride, ldw, K, N, up_off, C, ldc, row_info, y);
+  } else {
+    hipLaunchKernelGGL((grouped_gemv_kernel<SWIGLU, FUSE, CPL, WAUX, 1>), dim3(unsigned(waves)), dim3(64), 0,
+                       stream, A, lda, gather_src, gather_k, gather_rows, offsets, E_local, capacity, W,
+                       w_expert_stride, ldw, K, N, up_off, C, ldc, row_info, y);
+  }
   return hipGetLastError();
 }
 

@@ -29,8 +29,9 @@ pytestmark = pytest.mark.gpu
     (64, 64, [2, 0, 16]),                       # 2 k-steps, one panel
     (32, 32, [16, 3, 0, 1]),                    # one k-step: every later ring slot reloads it
     (1024, 512, [9, 12, 1, 30, 0, 16, 7, 11]),  # several ring turns
-    (7168, 2048, [14, 9, 0, 16, 1, 33, 8, 12]), # the DeepSeek-R1 expert shape
-], ids=["ragged", "full16", "two_groups", "hot", "tiny", "one_step", "mid", "dsr1"])
+    (7168, 2048, [14, 9, 0, 16, 1, 33, 8, 12]), # the DeepSeek-R1 expert shape (one-wave workgroups)
+    (7168, 2048, [14, 9, 0, 16, 1, 33, 8, 12, 5, 20, 3, 7, 11, 2, 30, 4]),  # 512+ panels: four-wave workgroups
+], ids=["ragged", "full16", "two_groups", "hot", "tiny", "one_step", "mid", "dsr1", "dsr1_16"])
 def test_grouped_gemv_matches_tiles(H, I, counts):
     dev = device()
     E_local = len(counts)

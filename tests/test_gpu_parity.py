@@ -406,7 +406,7 @@ def test_empty_batch_is_noop():
 # the named workloads at their full sizes                                       #
 # --------------------------------------------------------------------------- #
 @pytest.mark.parametrize("name", ["small_top2", "gptoss20b_ep8_share", "gptoss20b_ep2_tp4_share", "dsr1_ep8_share",
-                                  "dsr1_ep8_decode", "dsr1_ep8_share_zipf"])
+                                  "dsr1_ep8_decode", "gptoss20b_ep8_decode", "dsr1_ep8_share_zipf"])
 def test_named_workload_full_size(name):
     cfg = W.CONFIGS[name]
     dev = device()

@@ -102,6 +102,9 @@ CONFIGS: dict[str, MoEConfig] = {
     "dsr1_ep8_decode": MoEConfig("dsr1_ep8_decode", T=256, H=7168, I=2048, E=256, k=8, e0=0, E_local=32,
                                  note="DeepSeek-R1-shaped layer, rank 0 of EP=8, one decode step of 256 "
                                       "tokens (about 8 rows per local expert)"),
+    "gptoss20b_ep8_decode": MoEConfig("gptoss20b_ep8_decode", T=256, H=2880, I=3072, E=32, k=4, e0=0, E_local=4,
+                                      note="GPT-OSS-20B-shaped layer, rank 0 of EP=8, one decode step of 256 "
+                                           "tokens (about 32 rows per local expert)"),
     "dsr1_ep8_share_zipf": MoEConfig("dsr1_ep8_share_zipf", T=16384, H=7168, I=2048, E=256, k=8,
                                      e0=0, E_local=32, zipf_s=1.2, zipf_kappa=1.0,
                                      note="DeepSeek-R1 shapes, Zipf(1.2)-skewed expert popularity"),
