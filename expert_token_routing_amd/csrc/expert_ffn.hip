@@ -594,7 +594,7 @@ hipError_t launch_panel(int64_t tiles, hipStream_t stream, const uint16_t* A, in
                         uint16_t* C, int ldc, int K, int N, int up_off, const int32_t* gather_src, int gather_k,
                         int gather_rows, const int2* row_info, uint16_t* y, int64_t rows_hint) {
   // With few rows per expert expected, the grouped GEMV takes every expert.
-  if (grouped_gemv_usable(rows_hint, K, SWIGLU))
+  if (grouped_gemv_usable(rows_hint, K, N, E_local, SWIGLU))
     return SWIGLU ? launch_grouped_gemv1(A, lda, gather_src, gather_k, gather_rows, offsets, E_local, capacity, W, K,
                                          N, C, stream)
                   : launch_grouped_gemv2(A, offsets, E_local, capacity, W, N, K, row_info, C, y, stream);

@@ -358,12 +358,15 @@ hipError_t launch(const uint16_t* A, int lda, const int32_t* gather_src, int gat
 
 }  // namespace gemv
 
-bool grouped_gemv_usable(int64_t rows_hint, int K, bool gate_up) {
-  // Measured against the tile kernel on DeepSeek-R1-shaped shares: the
-  // gate/up GEMM wins up to 16 expected rows per local expert (nearly every
-  // expert fits one wave of 32 rows; at 24 and 32 it lost), the down GEMM up
-  // to 32. K in whole steps.
-  return K % gemv::kStepK == 0 && rows_hint <= (gate_up ? gemv::kGroupRows / 2 : gemv::kGroupRows);
+bool grouped_gemv_usable(int64_t rows_hint, int K, int N, int E_local, bool gate_up) {
+  // Measured against the tile kernel: the down GEMM wins up to 32 expected
+  // rows per local expert; the gate/up GEMM up to 16 when the local experts
+  // have 512 panels or more (DeepSeek-R1 shapes: at 24 and 32 rows it lost)
+  // and up to 32 when they have fewer (GPT-OSS-20B decode step, 4 experts x
+  // 48 panels at 32 rows: 40 against 50 us). K in whole steps.
+  const int64_t panels = int64_t(E_local) * ceil_div(N, gate_up ? 64 : 128);
+  const int64_t limit = gate_up && panels >= 512 ? gemv::kGroupRows / 2 : gemv::kGroupRows;
+  return K % gemv::kStepK == 0 && rows_hint <= limit;
 }
 
 hipError_t launch_grouped_gemv1(const uint16_t* A, int lda, const int32_t* gather_src, int gather_k, int gather_rows,

@@ -64,8 +64,9 @@ hipError_t launch_expert_gemm2_fused(const uint16_t* h, const int32_t* offsets, 
 // of one expert for up to 32 of its rows (an expert with more gets more
 // waves). Usable when K (H for the gate/up GEMM, I for the down GEMM) is a
 // multiple of 32; chosen when the expected rows per local expert
-// (rows_hint) are at most 16 (gate/up GEMM) or 32 (down GEMM).
-bool grouped_gemv_usable(int64_t rows_hint, int K, bool gate_up);
+// (rows_hint) are at most 32 (gate/up GEMM with 512 panels or more: 16).
+// N: outputs (I for the gate/up GEMM, H for the down GEMM).
+bool grouped_gemv_usable(int64_t rows_hint, int K, int N, int E_local, bool gate_up);
 // gate/up + SwiGLU: rows from A [.., H] (row n of a segment is row
 // gather_src[n] / gather_k of A when gather_src is given) into h [capacity, I]
 hipError_t launch_grouped_gemv1(const uint16_t* A, int lda, const int32_t* gather_src, int gather_k, int gather_rows,
