@@ -367,9 +367,14 @@ int route_k_parts(int T, int H, int E) {
   const int nk_all = H / routedma::kSK;
   const int64_t tiles = int64_t((T + routedma::kBM - 1) / routedma::kBM) * ((E + routedma::kBN - 1) / routedma::kBN);
   // enough parts for about 256 workgroups, at least 2, each part at least 4
-  // stages deep; then as few parts as that depth needs
+  // stages deep (1 when the T x E partial sums the top-k kernel adds are
+  // small: measured on decode steps, a GPT-OSS-20B-shaped one, T E = 8K,
+  // routes in 19 instead of 22 us at one stage per part, a DeepSeek-R1-shaped
+  // one, T E = 64K, in 37 instead of 29); then as few parts as that depth
+  // needs
   int64_t want = std::max<int64_t>(2, (256 + tiles - 1) / std::max<int64_t>(tiles, 1));
-  want = std::min<int64_t>(want, std::max(2, nk_all / 4));
+  const int min_depth = int64_t(T) * E <= 16384 ? 1 : 4;
+  want = std::min<int64_t>(want, std::max(2, nk_all / min_depth));
   want = std::min<int64_t>(want, nk_all);
   if (want < 2) return 1;
   const int per = int((nk_all + want - 1) / want);

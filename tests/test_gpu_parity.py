@@ -69,7 +69,7 @@ SMALL_CASES = [
     ragged("dma_half_stage", T=700, H=160, I=224, E=8, k=2, e0=2, E_local=4),
     # few tokens for a long hidden dimension: the router's k range in 4 parts
     # (19 stages of 64: 5 + 5 + 5 + 4)
-    ragged("route_parts", T=200, H=1216, I=96, E=40, k=4, e0=8, E_local=8),
+    ragged("route_parts", T=500, H=1216, I=96, E=40, k=4, e0=8, E_local=8),
     # more tokens than one dispatch workgroup takes, H off the 32 grid: the
     # forward copies rows with placement fused into the copy
     ragged("copy_placed", T=1100, H=200, I=136, E=12, k=3, e0=4, E_local=5),
