@@ -278,8 +278,15 @@ struct ALoaderP {
   }
 };
 
+// Block (kq, nq) of a B stage sits at 128 (kq * kNQ + (nq ^ b_swz(kq))): the
+// four 16-lane groups of a transposing read take blocks kq = 2 g (+1) of one
+// nq, and the LDS serves groups 0, 1 (and 2, 3) in one pass; unswizzled their
+// blocks are 4 KiB apart on the same 32 banks, swizzled they sit on the two
+// halves of the 64 banks.
+__device__ __forceinline__ int b_swz(int kq) { return (kq >> 1) & 1; }
+
 // B stage: kSK k x kBN columns of an n-contiguous matrix, 4 x 16 blocks of
-// 128 bytes at 128 (kq * kNQ + nq); load j of wave w fills blocks
+// 128 bytes (swizzled as above); load j of wave w fills block positions
 // 8 (j * 8 + w) .. +7.
 struct BLoaderP {
   static constexpr int kPer = kSK / 4 * kNQ / 8 / kWaves;
@@ -295,7 +302,7 @@ struct BLoaderP {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int blk = 8 * (j * kWaves + w) + (lane >> 3);
-      const int kq = blk / kNQ, nq = blk % kNQ;
+      const int kq = blk / kNQ, nq = (blk % kNQ) ^ b_swz(kq);
       const int r = (lane & 7) >> 1, c = lane & 1;
       voff[j] = uint32_t(4 * kq + r) * uint32_t(ldw) * 2u + 2u * uint32_t(col_of(16 * nq + 8 * c));
     }
@@ -324,15 +331,21 @@ struct BLoaderP {
 //    change), so one base per k step plus 16 kWR kRowBytes i.
 // B: fragment j = columns 64 wn + 16 j; lane group g = l >> 4 takes k
 //    32 q + 8g .. +7 from blocks (8 q + 2g, nq) and (8 q + 2g + 1, nq).
+// B fragment j of group g is block column 4 wn + (j ^ b_swz(2 g)) (b_swz of
+// 2 g and 2 g + 1 agree, and so do those of the k steps' 8 q + 2 g): even
+// fragments at b_e + 128 j, odd ones at b_o + 128 j.
 struct FragAddrP {
   uint32_t a[kSub];
-  uint32_t b;
+  uint32_t b_e, b_o;
   __device__ __forceinline__ void init(int wm, int wn) {
     const int lane = lane_id();
     const int r = 16 * wm + (lane & 15);
 #pragma unroll
     for (int q = 0; q < kSub; ++q) a[q] = uint32_t(r * kRowBytes + 16 * a_chunk_pos(r, 4 * q + (lane >> 4)));
-    b = uint32_t((2 * (lane >> 4) * kNQ + 4 * wn) * 128 + 8 * (lane & 15));
+    const uint32_t b = uint32_t((2 * (lane >> 4) * kNQ + 4 * wn) * 128 + 8 * (lane & 15));
+    const uint32_t sw = uint32_t(128 * b_swz(2 * (lane >> 4)));
+    b_e = b + sw;
+    b_o = b - sw;
   }
 };
 
@@ -342,7 +355,7 @@ __device__ __forceinline__ u32x4 read_a(const MOE_LDS char* As, const FragAddrP&
 }
 template <int Q>
 __device__ __forceinline__ u32x4 read_b(const MOE_LDS char* Bs, const FragAddrP& fa, int j) {
-  const MOE_LDS char* p0 = Bs + fa.b + Q * 8 * kNQ * 128 + 128 * j;
+  const MOE_LDS char* p0 = Bs + ((j & 1) ? fa.b_o : fa.b_e) + Q * 8 * kNQ * 128 + 128 * j;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4*)(p0));
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4*)(p0 + kNQ * 128));
   const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
