@@ -79,7 +79,8 @@ static ForwardLayout forward_layout(int T, int H, int I, int E, int k, int E_loc
   L.perm_src = take(size_t(cap) * sizeof(int32_t));
   L.inv = take(size_t(T) * k * sizeof(int32_t));
   L.chunks = take(dispatch_table_bytes(T, E));
-  L.x_perm = take(size_t(cap) * H * sizeof(uint16_t));
+  // the dispatched rows: only when GEMM1 cannot read the token vectors in place
+  L.x_perm = take(expert_gemm1_can_gather(T, H) ? 0 : size_t(cap) * H * sizeof(uint16_t));
   L.h = take(size_t(cap) * I * sizeof(uint16_t));
   L.out = take(size_t(cap) * H * sizeof(uint16_t));
   L.row_info = take(size_t(cap) * sizeof(int2));

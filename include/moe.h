@@ -277,7 +277,9 @@ int moe_forward_fused_profiled(const moe_bf16* x, const float* w_router, const f
  * Byte offsets of the intermediates inside the moe_forward workspace, so a
  * caller can read them after the call (for checks and measurements). Writes
  * 9 values into `offsets_out` (host memory): logits, topk_idx, topk_w, counts,
- * offsets, perm_src, inv, x_perm, expert_out. Returns MOE_OK or
+ * offsets, perm_src, inv, x_perm, expert_out. The x_perm region is empty
+ * (the forward's gate/up GEMM reads the token vectors of x in place) unless
+ * H is not a multiple of 32 or T * H * 2 >= 2^31. Returns MOE_OK or
  * MOE_ERR_INVALID_ARG.
  */
 int moe_forward_workspace_layout(int T, int H, int I, int E, int k, int E_local,

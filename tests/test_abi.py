@@ -43,14 +43,27 @@ def test_workspace_sizes():
     assert L.moe_dispatch_workspace_size(16384, 256, 8) >= 256 * 256 * 4
     assert L.moe_dispatch_workspace_size(1, 4, 1) >= 16
     T, H, I, E, k, El = 16384, 7168, 2048, 256, 8, 32
+    # the gate/up GEMM reads the token vectors in place (H a multiple of 32,
+    # T*H*2 < 2^31): no dispatched copy x_perm in the workspace
     ws = M.forward_workspace_size(T, H, I, E, k, El)
     cap = T * min(k, El)
-    assert ws >= cap * H * 2 * 2 + cap * I * 2 + T * E * 4
+    assert cap * H * 2 + cap * I * 2 + T * E * 4 <= ws < 2 * cap * H * 2
     lay = M.forward_workspace_layout(T, H, I, E, k, El)
     offs = sorted(lay.values())
     assert all(o % 256 == 0 for o in offs)
     assert len(set(offs)) == len(offs) and offs[-1] < ws
     assert lay["expert_out"] + cap * H * 2 <= ws
+    assert lay["expert_out"] - lay["x_perm"] == cap * I * 2  # x_perm empty, h between
+    # H not a multiple of 32: the rows are copied out first, x_perm takes cap x H
+    H2 = 7176
+    ws2 = M.forward_workspace_size(T, H2, I, E, k, El)
+    lay2 = M.forward_workspace_layout(T, H2, I, E, k, El)
+    assert ws2 >= 2 * cap * H2 * 2 + cap * I * 2 + T * E * 4
+    assert lay2["expert_out"] - lay2["x_perm"] >= cap * H2 * 2 + cap * I * 2
+    # T*H*2 >= 2^31 also copies the rows out
+    T3 = 150000
+    lay3 = M.forward_workspace_layout(T3, H, I, E, k, El)
+    assert lay3["expert_out"] - lay3["x_perm"] >= T3 * min(k, El) * H * 2
     assert L.moe_forward_workspace_size(-1, H, I, E, k, El) == 0
 
 
@@ -162,3 +175,4 @@ def _forward(name="moe_forward", **kw):
 @pytest.mark.parametrize("name", ["moe_forward", "moe_forward_f32", "moe_forward_fused"])
 def test_forward_rejects(name, kw, want):
     assert _forward(name, **kw) == want
+
