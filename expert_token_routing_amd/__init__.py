@@ -6,7 +6,9 @@ original token order), all in hand-written gfx950 HIP kernels behind the
 C-ABI of ``include/moe.h``; this package is its Python binding.
 """
 from ._binding import (  # noqa: F401
-    LIB_PATH, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_OK, SIGNATURES,
+    LIB_PATH, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_OK,
+    NOALLOC_SCRATCH_BYTES, SIGNATURES,
     MoEError, check, forward_workspace_layout, forward_workspace_size, lib, moe_combine, moe_combine_f32, moe_dispatch,
-    moe_expert_ffn, moe_forward, moe_forward_f32, moe_forward_fused, moe_forward_profiled, moe_route, status_string,
+    moe_expert_ffn, moe_forward, moe_forward_f32, moe_forward_fused, moe_forward_noalloc, moe_forward_profiled, moe_route,
+    status_string,
 )

@@ -42,7 +42,12 @@ SIGNATURES = {
                                   _P, _P, c_size_t, _P]),
     "moe_forward_fused_profiled": (c_int, [_P, _P, _P, _P, _P, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                            c_int, _P, _P, c_size_t, _P, _P]),
+    "moe_forward_noalloc": (c_int, [_P, _P, _P, _P, _P, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                    _P, _P]),
 }
+
+# bytes of the static scratch moe_forward_noalloc works in (MOE_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 _lib = None
 
@@ -287,3 +292,27 @@ def moe_forward_profiled(x, w_router, bias, w_gate_up, w_down, k, e0, renormaliz
                               k, e0, E_local, int(bool(renormalize)), _ptr(y), _ptr(workspace), workspace.numel(),
                               arr, _stream(stream, x.device))
     check(st, name)
+
+
+def moe_forward_noalloc(x, w_router, bias, w_gate_up, w_down, k, e0, renormalize=True, *, y, stream=None):
+    """moe_forward with the intermediates in the library's static scratch
+    (no workspace; the call allocates nothing on the device). ``y`` [T, H]
+    bf16 is the caller's. Raises MoEError(MOE_ERR_WORKSPACE) when the problem
+    needs more than NOALLOC_SCRATCH_BYTES."""
+    torch = _torch()
+    _need(x, torch.bfloat16, "x", 2)
+    _need(w_router, torch.float32, "w_router", 2)
+    if bias is not None:
+        _need(bias, torch.float32, "bias", 1)
+    _need(w_gate_up, torch.bfloat16, "w_gate_up", 3)
+    _need(w_down, torch.bfloat16, "w_down", 3)
+    _need(y, torch.bfloat16, "y", 2)
+    T, H = x.shape
+    E = w_router.shape[0]
+    E_local, _, I2 = w_gate_up.shape
+    if tuple(y.shape) != (T, H):
+        raise ValueError(f"y must have shape {(T, H)}, got {tuple(y.shape)}")
+    st = lib().moe_forward_noalloc(_ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate_up), _ptr(w_down), T, H, I2 // 2,
+                                   E, k, e0, E_local, int(bool(renormalize)), _ptr(y), _stream(stream, x.device))
+    check(st, "moe_forward_noalloc")
+    return y

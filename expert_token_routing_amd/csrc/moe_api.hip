@@ -18,7 +18,29 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 std::mutex g_dev_mu;
 int g_cu_count[64] = {0};
+void* g_scratch_ptr[64] = {nullptr};
 }  // namespace
+
+// The forward workspace of moe_forward_noalloc, for callers that cannot
+// allocate. Each GPU the library runs on holds its own copy, from the load
+// of the library's code on that GPU until the process ends.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+// This device's address of `scratch`, looked up once per device with the
+// device current (the array's name is not a device address in host code).
+static int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ERR_HIP;
+  if (dev >= 64) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
 
 int device_cu_count() {
   int dev = 0;
@@ -272,6 +294,22 @@ int moe_forward(const moe_bf16* x, const float* w_router, const float* bias, con
                 moe_bf16* y, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return forward_impl(x, w_router, bias, w_gate_up, w_down, T, H, I, E, k, e0, E_local, renormalize, y, false,
                       workspace, workspace_bytes, nullptr, stream);
+}
+
+int moe_forward_noalloc(const moe_bf16* x, const float* w_router, const float* bias, const moe_bf16* w_gate_up,
+                        const moe_bf16* w_down, int T, int H, int I, int E, int k, int e0, int E_local, int renormalize,
+                        moe_bf16* y, hipStream_t stream) {
+  // the argument checks first, so that a rejected call has no side effect
+  int st = check_route_dims(T, H, E, k);
+  if (st != MOE_OK) return st;
+  if ((st = check_local(E, e0, E_local)) != MOE_OK) return st;
+  if (I <= 0 || (I % 8) != 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (forward_layout(T, H, I, E, k, E_local).total > size_t(MOE_NOALLOC_SCRATCH_BYTES)) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != MOE_OK) return st;
+  return forward_impl(x, w_router, bias, w_gate_up, w_down, T, H, I, E, k, e0, E_local, renormalize, y, false, ws,
+                      size_t(MOE_NOALLOC_SCRATCH_BYTES), nullptr, stream);
 }
 
 int moe_forward_f32(const moe_bf16* x, const float* w_router, const float* bias, const moe_bf16* w_gate_up,

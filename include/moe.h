@@ -217,6 +217,33 @@ int moe_forward(const moe_bf16* x, const float* w_router, const float* bias,
                 size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * moe_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The caller passes inputs and y as for moe_forward; the intermediates live
+ * in a static device array of MOE_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends, so no workspace is
+ * passed and the call allocates nothing.
+ *   - MOE_ERR_WORKSPACE (nothing launched) when the problem needs more than
+ *     the array holds, i.e. moe_forward_workspace_size(T, H, I, E, k,
+ *     E_local) > MOE_NOALLOC_SCRATCH_BYTES (a DeepSeek-R1-shaped EP=8 rank
+ *     share needs about 56 MB at T = 256 tokens, 192 MB at T = 1024).
+ *   - the array is shared by every call on one GPU and keeps the last call's
+ *     contents; no part of it needs to start at zero. Calls that overlap on
+ *     one GPU (two streams, two threads) race on it and must be ordered by
+ *     the caller.
+ *   - the first call on a device looks up that device's copy
+ *     (hipGetSymbolAddress); a caller that captures a graph may make one
+ *     call before capturing.
+ * Other arguments, checks and results are moe_forward's; y equals
+ * moe_forward's y bit for bit.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int moe_forward_noalloc(const moe_bf16* x, const float* w_router, const float* bias,
+                        const moe_bf16* w_gate_up, const moe_bf16* w_down, int T, int H, int I,
+                        int E, int k, int e0, int E_local, int renormalize, moe_bf16* y,
+                        hipStream_t stream);
+
+/*
  * moe_forward whose share y [T, H] is float32 (the partial-output form of
  * moe_combine_f32, same citation): every step is moe_forward's, only the
  * combine stores its float32 sums unrounded. Rounding y to bf16 gives

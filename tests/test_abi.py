@@ -176,3 +176,18 @@ def _forward(name="moe_forward", **kw):
 def test_forward_rejects(name, kw, want):
     assert _forward(name, **kw) == want
 
+
+def test_noalloc_host_checks():
+    """moe_forward_noalloc rejects bad arguments and problems larger than its
+    static scratch on the host, before it looks up the device array."""
+    L = M.lib()
+    assert B.NOALLOC_SCRATCH_BYTES == 128 << 20
+    args = [FAKE, FAKE, None, FAKE, FAKE]
+    # T, H, I, E, k, e0, E_local, renormalize, y, stream
+    assert L.moe_forward_noalloc(*args, 16, 64, 32, 8, 0, 0, 4, 1, FAKE, None) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_noalloc(*args, 16, 64, 32, 8, 2, 6, 4, 1, FAKE, None) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_noalloc(*args, 16, 64, 30, 8, 2, 0, 4, 1, FAKE, None) == M.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_noalloc(*args, 0, 64, 32, 8, 2, 0, 4, 1, FAKE, None) == M.MOE_OK
+    T, H, I, E, k, El = 16384, 7168, 2048, 256, 8, 32
+    assert L.moe_forward_workspace_size(T, H, I, E, k, El) > B.NOALLOC_SCRATCH_BYTES
+    assert L.moe_forward_noalloc(*args, T, H, I, E, k, 0, El, 1, FAKE, None) == M.MOE_ERR_WORKSPACE
