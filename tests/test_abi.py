@@ -191,3 +191,121 @@ def test_noalloc_host_checks():
     T, H, I, E, k, El = 16384, 7168, 2048, 256, 8, 32
     assert L.moe_forward_workspace_size(T, H, I, E, k, El) > B.NOALLOC_SCRATCH_BYTES
     assert L.moe_forward_noalloc(*args, T, H, I, E, k, 0, El, 1, FAKE, None) == M.MOE_ERR_WORKSPACE
+
+
+# --------------------------------------------------------------------------- #
+# The Python binding checks every tensor's dtype and shape before any launch:  #
+# the library sees only pointers, so a wrong size would otherwise become an    #
+# out-of-bounds access on the GPU. Shapes are checked before the device, so    #
+# these CPU tensors are rejected for their shapes.                             #
+# --------------------------------------------------------------------------- #
+def _fwd_tensors(T=16, H=64, I=32, E=8, El=4):
+    import torch
+    bf = torch.bfloat16
+    return dict(x=torch.zeros(T, H, dtype=bf), w_router=torch.zeros(E, H), bias=torch.zeros(E),
+                w_gate_up=torch.zeros(El, H, 2 * I, dtype=bf), w_down=torch.zeros(El, I, H, dtype=bf))
+
+
+@pytest.mark.parametrize("fn", ["moe_forward", "moe_forward_f32", "moe_forward_fused"])
+@pytest.mark.parametrize("bad,match", [
+    ("w_router", "w_router has shape"), ("bias", "bias has shape"), ("w_gate_up", "w_gate_up has shape"),
+    ("w_down", "w_down has shape"), ("y", "y has shape"), ("k", "k must be"), ("e0", "local experts")])
+def test_forward_rejects_mismatched_shapes(fn, bad, match):
+    import torch
+    t = _fwd_tensors()
+    kw = dict(k=2, e0=0)
+    if bad == "w_router":
+        t["w_router"] = torch.zeros(8, 72)
+    elif bad == "bias":
+        t["bias"] = torch.zeros(9)
+    elif bad == "w_gate_up":
+        t["w_gate_up"] = torch.zeros(4, 56, 64, dtype=torch.bfloat16)
+    elif bad == "w_down":
+        t["w_down"] = torch.zeros(4, 32, 72, dtype=torch.bfloat16)
+    elif bad == "y":
+        kw["y"] = torch.zeros(16, 72, dtype=torch.float32 if fn == "moe_forward_f32" else torch.bfloat16)
+    elif bad == "k":
+        kw["k"] = 9
+    elif bad == "e0":
+        kw["e0"] = 5
+    with pytest.raises(ValueError, match=match):
+        getattr(M, fn)(t["x"], t["w_router"], t["bias"], t["w_gate_up"], t["w_down"], **kw)
+
+
+def test_forward_rejects_wrong_dtype_and_device():
+    import torch
+    t = _fwd_tensors()
+    with pytest.raises(TypeError, match="w_router must be"):
+        M.moe_forward(t["x"], t["w_router"].double(), None, t["w_gate_up"], t["w_down"], 2, 0)
+    with pytest.raises(ValueError, match="must live on a GPU"):
+        M.moe_forward(t["x"], t["w_router"], None, t["w_gate_up"], t["w_down"], 2, 0)
+
+
+def test_noalloc_and_profiled_reject_mismatched_shapes():
+    import torch
+    t = _fwd_tensors()
+    with pytest.raises(ValueError, match="y has shape"):
+        M.moe_forward_noalloc(t["x"], t["w_router"], None, t["w_gate_up"], t["w_down"], 2, 0,
+                              y=torch.zeros(15, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="w_down has shape"):
+        M.moe_forward_profiled(t["x"], t["w_router"], None, t["w_gate_up"], torch.zeros(4, 31, 64, dtype=torch.bfloat16),
+                               2, 0, True, torch.zeros(16, 64, dtype=torch.bfloat16), torch.zeros(16, dtype=torch.uint8),
+                               [None] * 6)
+
+
+def test_route_rejects_mismatched_shapes():
+    import torch
+    x = torch.zeros(16, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="w_router has shape"):
+        M.moe_route(x, torch.zeros(8, 32), None, 2)
+    with pytest.raises(ValueError, match="bias has shape"):
+        M.moe_route(x, torch.zeros(8, 64), torch.zeros(7), 2)
+    with pytest.raises(ValueError, match="k must be"):
+        M.moe_route(x, torch.zeros(8, 64), None, 0)
+    for name, bad in (("logits", torch.zeros(16, 7)), ("topk_idx", torch.zeros(16, 3, dtype=torch.int32)),
+                      ("topk_w", torch.zeros(15, 2))):
+        with pytest.raises(ValueError, match=f"{name} has shape"):
+            M.moe_route(x, torch.zeros(8, 64), None, 2, **{name: bad})
+
+
+def test_dispatch_rejects_mismatched_shapes():
+    import torch
+    x = torch.zeros(16, 64, dtype=torch.bfloat16)
+    idx = torch.zeros(16, 2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="topk_idx has shape"):
+        M.moe_dispatch(x, torch.zeros(15, 2, dtype=torch.int32), 8, 0, 4)
+    with pytest.raises(ValueError, match="local experts"):
+        M.moe_dispatch(x, idx, 8, 6, 4)
+    with pytest.raises(ValueError, match="capacity"):
+        M.moe_dispatch(x, idx, 8, 0, 4, capacity=31)
+    for name, bad in (("counts", torch.zeros(7, dtype=torch.int32)), ("offsets", torch.zeros(4, dtype=torch.int32)),
+                      ("perm_src", torch.zeros(31, dtype=torch.int32)), ("inv", torch.zeros(31, dtype=torch.int32)),
+                      ("x_perm", torch.zeros(32, 56, dtype=torch.bfloat16))):
+        with pytest.raises(ValueError, match=f"{name} has shape"):
+            M.moe_dispatch(x, idx, 8, 0, 4, **{name: bad})
+
+
+def test_expert_ffn_and_combine_reject_mismatched_shapes():
+    import torch
+    bf = torch.bfloat16
+    xp = torch.zeros(32, 64, dtype=bf)
+    gu = torch.zeros(4, 64, 64, dtype=bf)
+    dn = torch.zeros(4, 32, 64, dtype=bf)
+    off = torch.zeros(5, dtype=torch.int32)
+    with pytest.raises(ValueError, match="w_gate_up has shape"):
+        M.moe_expert_ffn(xp, off, torch.zeros(4, 72, 64, dtype=bf), dn)
+    with pytest.raises(ValueError, match="w_down has shape"):
+        M.moe_expert_ffn(xp, off, gu, torch.zeros(4, 32, 72, dtype=bf))
+    with pytest.raises(ValueError, match="offsets has shape"):
+        M.moe_expert_ffn(xp, torch.zeros(4, dtype=torch.int32), gu, dn)
+    with pytest.raises(ValueError, match="h has shape"):
+        M.moe_expert_ffn(xp, off, gu, dn, h=torch.zeros(32, 31, dtype=bf))
+    with pytest.raises(ValueError, match="out has shape"):
+        M.moe_expert_ffn(xp, off, gu, dn, out=torch.zeros(31, 64, dtype=bf))
+    w = torch.zeros(16, 2)
+    with pytest.raises(ValueError, match="inv has shape"):
+        M.moe_combine(xp, torch.zeros(31, dtype=torch.int32), w)
+    with pytest.raises(ValueError, match="y has shape"):
+        M.moe_combine(xp, torch.zeros(32, dtype=torch.int32), w, y=torch.zeros(16, 56, dtype=bf))
+    with pytest.raises(ValueError, match="y has shape"):
+        M.moe_combine_f32(xp, torch.zeros(32, dtype=torch.int32), w, y=torch.zeros(15, 64))

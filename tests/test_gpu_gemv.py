@@ -1,9 +1,10 @@
 """The grouped GEMV (experts with at most 32 rows) against the tile kernel.
 
-moe_expert_ffn picks the GEMV when its capacity averages at most 16 rows per
-local expert, so the same rows run through both kernels by passing them once
-in a buffer of exactly their size and once padded to more than 64 rows per
-expert (rows past offsets[E_local] are never read). Every output element is
+moe_expert_ffn picks the GEMV when its capacity averages at most 32 rows per
+local expert (for a gate/up GEMM whose local experts have 512 panels of 64
+outputs or more: at most 16), so the same rows run through both kernels by
+passing them once in a buffer of exactly their size and once padded to more
+than 64 rows per expert (rows past offsets[E_local] are never read). Every output element is
 one MFMA chain over k in the same order in both kernels, so h and the expert
 outputs must agree bit for bit. Inputs are drawn on the GPU; this compares
 two paths of the library, the oracle comparisons of the same kernels are in
@@ -31,13 +32,22 @@ pytestmark = pytest.mark.gpu
     (1024, 512, [9, 12, 1, 30, 0, 16, 7, 11]),  # several ring turns
     (7168, 2048, [14, 9, 0, 16, 1, 33, 8, 12]), # the DeepSeek-R1 expert shape (one-wave workgroups)
     (7168, 2048, [14, 9, 0, 16, 1, 33, 8, 12, 5, 20, 3, 7, 11, 2, 30, 4]),  # 512+ panels: four-wave workgroups
-], ids=["ragged", "full16", "two_groups", "hot", "tiny", "one_step", "mid", "dsr1", "dsr1_16"])
+    # 17..32 expected rows per expert: both GEMMs on the GEMV while the gate/up
+    # panels are fewer than 512 (rows 16 / 17 / 31 / 32 / 33 at the group
+    # edges, ragged 64-column gate/up and 128-column down panels)
+    (224, 160, [16, 17, 31, 32, 33, 20, 25, 18]),
+    (256, 96, [32, 32, 32, 32]),                # exactly 32 rows everywhere (two full groups)
+    (2880, 3072, [40, 24, 31, 33]),             # GPT-OSS-20B expert shape, few panels, 32 expected rows
+    # 17..32 expected rows with 512 gate/up panels: gate/up on tiles, down on the GEMV
+    (1024, 2048, [20, 17, 31, 0, 33, 16, 25, 18, 22, 19, 32, 1, 21, 24, 30, 27]),
+], ids=["ragged", "full16", "two_groups", "hot", "tiny", "one_step", "mid", "dsr1", "dsr1_16", "edges17_33", "full32",
+        "gptoss", "down_only"])
 def test_grouped_gemv_matches_tiles(H, I, counts):
     dev = device()
     E_local = len(counts)
     N = int(sum(counts))
     cap_big = 64 * E_local + 1
-    assert N <= 16 * E_local
+    assert N <= 32 * E_local
     g = torch.Generator(device=dev).manual_seed(11)
     x = (torch.randn((cap_big, H), generator=g, device=dev) / H ** 0.5).to(torch.bfloat16)
     wgu = (torch.randn((E_local, H, 2 * I), generator=g, device=dev) / H ** 0.5).to(torch.bfloat16)
