@@ -47,7 +47,7 @@ import numpy as np
 __all__ = [
     "bf16_to_f64", "oracle_logits", "oracle_topk", "oracle_weights", "oracle_route",
     "oracle_counts", "oracle_offsets", "oracle_permutation", "oracle_gather",
-    "oracle_dispatch", "oracle_silu", "oracle_expert_mlp", "oracle_expert_ffn",
+    "oracle_dispatch", "oracle_silu", "oracle_expert_h", "oracle_expert_mlp", "oracle_expert_ffn",
     "oracle_combine", "oracle_forward", "oracle_dense_forward",
 ]
 
@@ -184,17 +184,22 @@ def oracle_silu(z) -> np.ndarray:
         return z / (1.0 + np.exp(-z))
 
 
-def oracle_expert_mlp(xrows, w_gate_up, w_down) -> np.ndarray:
-    """One expert's SwiGLU MLP on stacked rows [M, H]:
-    g = X Wg, u = X Wu, h = silu(g) * u, out = h Wd, where Wg / Wu are the
-    first / last I columns of gate_up [H, 2I] and down is [I, H]."""
+def oracle_expert_h(xrows, w_gate_up) -> np.ndarray:
+    """The hidden rows of one expert's SwiGLU MLP on stacked rows [M, H]:
+    g = X Wg, u = X Wu, h = silu(g) * u, float64 [M, I], where Wg / Wu are
+    the first / last I columns of gate_up [H, 2I]."""
     X = _f64(xrows)
     Wgu = _f64(w_gate_up)
     I = Wgu.shape[1] // 2
     g = X @ Wgu[:, :I]
     u = X @ Wgu[:, I:]
-    h = oracle_silu(g) * u
-    return h @ _f64(w_down)
+    return oracle_silu(g) * u
+
+
+def oracle_expert_mlp(xrows, w_gate_up, w_down) -> np.ndarray:
+    """One expert's SwiGLU MLP on stacked rows [M, H]: out = h Wd with h of
+    oracle_expert_h and down [I, H]."""
+    return oracle_expert_h(xrows, w_gate_up) @ _f64(w_down)
 
 
 def oracle_expert_ffn(x_perm, offsets, w_gate_up, w_down) -> np.ndarray:

@@ -278,6 +278,28 @@ def pin_ffn_hand_example():
     assert np.allclose(out[0], [3.0 * h, -h], rtol=1e-15, atol=0), out
 
 
+def pin_expert_h_hand_example():
+    """H = 3, I = 2 worked by hand (gate and up blocks of different shapes
+    than the down matrix, so a transposed operand cannot pass):
+    x = [1, -2, 0.5];
+    gate columns [1, 0, 2] and [0, 0, 0] give g = [2, 0];
+    up columns [0, 1, 0] and [1, 1, 1] give u = [-2, -0.5];
+    h = [silu(2) * -2, silu(0) * -0.5] = [-4 / (1 + e^-2), 0].
+    A second row x = [0, 1, 0] gives g = [0, 0], u = [1, 1], h = [0, 0]."""
+    x = np.asarray([[1.0, -2.0, 0.5], [0.0, 1.0, 0.0]])
+    w_gu = np.asarray([[1.0, 0.0, 0.0, 1.0],
+                       [0.0, 0.0, 1.0, 1.0],
+                       [2.0, 0.0, 0.0, 1.0]])          # [H=3, 2I=4]: cols 0-1 gate, 2-3 up
+    h = O.oracle_expert_h(x, w_gu)
+    assert h.shape == (2, 2), h.shape
+    want0 = -4.0 / (1.0 + math.exp(-2.0))
+    assert math.isclose(h[0, 0], want0, rel_tol=1e-15), h
+    assert h[0, 1] == 0.0 and h[1, 0] == 0.0 and h[1, 1] == 0.0, h
+    # with gate = up, h = silu(g) * g: g = 2 gives 4 / (1 + e^-2)
+    w_same = np.concatenate([w_gu[:, :2], w_gu[:, :2]], axis=1)
+    assert math.isclose(O.oracle_expert_h(x[:1], w_same)[0, 0], -want0, rel_tol=1e-15)
+
+
 def _random_share_problem(seed, T, H, I, E, k, scale=1.0):
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((T, H)) * scale
@@ -409,6 +431,6 @@ def pin_bf16_decode():
 ALL_PINS = [
     pin_walkthrough_top1, pin_imbalance_top1, pin_top2_weighted_sum, pin_top4_partial_sums,
     pin_logits_bruteforce, pin_topk_bruteforce, pin_softmax_closed_form, pin_ffn_closed_form,
-    pin_ffn_hand_example, pin_dispatch_invariants, pin_identity_roundtrip, pin_sum_of_shares, pin_sum_of_ep_tp_shares,
+    pin_ffn_hand_example, pin_expert_h_hand_example, pin_dispatch_invariants, pin_identity_roundtrip, pin_sum_of_shares, pin_sum_of_ep_tp_shares,
     pin_dense_equals_grouped, pin_row_independence, pin_bf16_decode,
 ]

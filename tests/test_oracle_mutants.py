@@ -85,6 +85,25 @@ def _mlp_interleaved(xrows, w_gate_up, w_down):
     return _orig["oracle_expert_mlp"](xrows, np.concatenate([W[:, 0::2], W[:, 1::2]], axis=1), w_down)
 
 
+def _h_gate_up_swapped(xrows, w_gate_up):
+    W = O._f64(w_gate_up)
+    I = W.shape[1] // 2
+    return _orig["oracle_expert_h"](xrows, np.concatenate([W[:, I:], W[:, :I]], axis=1))
+
+
+def _h_no_up(xrows, w_gate_up):
+    W = O._f64(w_gate_up)
+    I = W.shape[1] // 2
+    return O.oracle_silu(O._f64(xrows) @ W[:, :I])
+
+
+def _h_silu_of_product(xrows, w_gate_up):
+    W = O._f64(w_gate_up)
+    I = W.shape[1] // 2
+    X = O._f64(xrows)
+    return O.oracle_silu((X @ W[:, :I]) * (X @ W[:, I:]))
+
+
 def _silu_sigmoid(z):
     z = np.asarray(z, np.float64)
     return 1.0 / (1.0 + np.exp(-z))
@@ -135,6 +154,9 @@ MUTANTS = {
     "dispatch: gather with modulo": ("oracle_gather", _gather_wrong_div),
     "mlp: gate and up swapped": ("oracle_expert_mlp", _mlp_gate_up_swapped),
     "mlp: interleaved gate/up": ("oracle_expert_mlp", _mlp_interleaved),
+    "h: gate and up swapped": ("oracle_expert_h", _h_gate_up_swapped),
+    "h: up projection dropped": ("oracle_expert_h", _h_no_up),
+    "h: silu of the product": ("oracle_expert_h", _h_silu_of_product),
     "mlp: sigmoid instead of silu": ("oracle_silu", _silu_sigmoid),
     "mlp: silu sign": ("oracle_silu", _silu_sign),
     "ffn: experts shifted": ("oracle_expert_ffn", _ffn_expert_shift),
