@@ -60,6 +60,49 @@ def rel_max_err(got: np.ndarray, ref: np.ndarray) -> float:
     return num / den
 
 
+# Row caps the panel GEMM picks from (largest first) and its column-tile width.
+PANEL_ROW_CAPS = (288, 256, 224, 192, 160, 128)
+PANEL_BN = 256
+
+
+def _cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def panel_blocks(seg_rows, n_out: int, gate_up: bool, capacity: int, cus: int):
+    """The row blocks the panel GEMM cuts the segments into, as the kernel
+    chooses them: for each row cap, the tile count (row blocks x column
+    tiles) and the tallest block; the cap minimising ceil(tiles / grid) x
+    (tallest + 256) wins, the larger on ties; a segment of m rows becomes
+    ceil(m / cap) blocks of equal height rounded up to 16 (the last one
+    shorter). Returns (cap, [(first row, end row)] over the whole row range).
+    n_out: the GEMM's output columns (I for gate/up, whose column tiles hold
+    128 outputs, H for down, 256); capacity: rows of the launch's buffers."""
+    ntn = _cdiv(n_out, PANEL_BN // 2 if gate_up else PANEL_BN)
+    seg = [int(m) for m in seg_rows]
+    bound = (_cdiv(capacity, PANEL_ROW_CAPS[-1]) + len(seg)) * ntn
+    grid = max(8, min(cus // 8 * 8, _cdiv(bound, 8) * 8))
+    best = None
+    for cap in PANEL_ROW_CAPS:
+        tiles = sum(_cdiv(m, cap) for m in seg if m > 0) * ntn
+        tallest = max([(_cdiv(m, _cdiv(m, cap)) + 15) // 16 * 16 for m in seg if m > 0], default=0)
+        est = _cdiv(tiles, grid) * (tallest + PANEL_BN)
+        if best is None or est < best[0]:
+            best = (est, cap)
+    cap = best[1]
+    blocks, start = [], 0
+    for m in seg:
+        if m > 0:
+            nrt = _cdiv(m, cap)
+            height = (_cdiv(m, nrt) + 15) // 16 * 16
+            for i in range(nrt):
+                r0 = i * height
+                if r0 < m:
+                    blocks.append((start + r0, start + min(m, r0 + height)))
+        start += m
+    return cap, blocks
+
+
 # Tolerance on expert outputs and the combined output: bf16 inputs and
 # weights, float32 accumulation, bf16 storage of h, the expert outputs and y.
 OUT_TOL = 2e-2

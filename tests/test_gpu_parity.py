@@ -19,8 +19,8 @@ import expert_token_routing_amd as M
 import oracle.moe_oracle as O
 import workloads as W
 from tests import oracle_pins as P
-from tests.gpu_helpers import (OUT_TOL, W_RTOL, DevInputs, bf16_bits, bf16_f64, device, rel_max_err, say,
-                               to_dev, to_dev_bf16)
+from tests.gpu_helpers import (OUT_TOL, W_RTOL, DevInputs, bf16_bits, bf16_f64, device, panel_blocks, rel_max_err,
+                               say, to_dev, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -156,22 +156,34 @@ def check_dispatch(cfg, inp, gi, res):
     return N, ro, rp, rinv
 
 
-def sample_rows(offsets, per_expert, rng):
-    """Rows to check: the first and last rows of each segment, rows around
-    m-tile boundaries, and a random draw."""
-    rows = []
+def sample_rows(offsets, per_expert, rng, blocks=()):
+    """Rows to check: the first and last rows of each segment, the edges of
+    the row blocks the GEMMs cut it into (`blocks`: (first, end) pairs) and
+    of the 16-row fragments beside them, and a random draw per segment."""
+    rows = set()
     E_local = len(offsets) - 1
+    for a, b in blocks:
+        rows.update(r for r in (a, a + 1, a + 15, a + 16, b - 17, b - 16, b - 2, b - 1) if a <= r < b)
     for i in range(E_local):
         a, b = int(offsets[i]), int(offsets[i + 1])
         if b <= a:
             continue
-        cand = {a, b - 1, min(b - 1, a + 127), min(b - 1, a + 128), min(b - 1, a + 255)}
+        rows.update((a, b - 1))
         if b - a > per_expert:
-            cand.update(rng.choice(np.arange(a, b), size=per_expert, replace=False).tolist())
+            rows.update(rng.choice(np.arange(a, b), size=per_expert, replace=False).tolist())
         else:
-            cand.update(range(a, b))
-        rows.extend(sorted(cand))
-    return np.asarray(sorted(set(rows)), dtype=np.int64)
+            rows.update(range(a, b))
+    return np.asarray(sorted(rows), dtype=np.int64)
+
+
+def gemm_blocks(cfg, ro, capacity):
+    """Row blocks of both grouped GEMMs of moe_expert_ffn for the realised
+    segments (the union of the two launches' splits)."""
+    seg = np.diff(np.asarray(ro)).tolist()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    _, b1 = panel_blocks(seg, cfg.I, True, capacity, cus)
+    _, b2 = panel_blocks(seg, cfg.H, False, capacity, cus)
+    return sorted(set(b1) | set(b2))
 
 
 def expert_of_rows(offsets, rows):
@@ -185,12 +197,19 @@ def check_ffn(cfg, inp, res, N, ro, rows=None):
     if rows.size == 0:
         return
     ex = expert_of_rows(ro, rows)
-    got = bf16_f64(out[torch.from_numpy(rows).to(out.device)])
-    xp = bf16_bits(res["x_perm"][torch.from_numpy(rows).to(out.device)])
+    sel_dev = torch.from_numpy(rows).to(out.device)
+    got = bf16_f64(out[sel_dev])
+    got_h = bf16_f64(res["h"][sel_dev])
+    xp = bf16_bits(res["x_perm"][sel_dev])
     ref = np.zeros_like(got)
+    ref_h = np.zeros_like(got_h)
     for i in np.unique(ex):
         sel = ex == i
+        ref_h[sel] = O.oracle_expert_h(xp[sel], inp.w_gate_up[i])
         ref[sel] = O.oracle_expert_mlp(xp[sel], inp.w_gate_up[i], inp.w_down[i])
+    # the gate/up GEMM's h on its own, then the expert outputs
+    err_h = rel_max_err(got_h, ref_h)
+    assert err_h <= OUT_TOL, ("h", err_h)
     err = rel_max_err(got, ref)
     assert err <= OUT_TOL, err
 
@@ -416,7 +435,7 @@ def test_named_workload_full_size(name):
     gl, gi, gw = check_route(cfg, inp, res["logits"], res["idx"], res["w"])
     N, ro, rp, rinv = check_dispatch(cfg, inp, gi, res)
     rng = np.random.default_rng(7)
-    rows = np.arange(N) if N <= 4096 else sample_rows(ro, 12, rng)
+    rows = np.arange(N) if N <= 4096 else sample_rows(ro, 12, rng, gemm_blocks(cfg, ro, res["x_perm"].shape[0]))
     check_ffn(cfg, inp, res, N, ro, rows)
     check_combine(cfg, res, gw, rinv)
     say(f"moe_forward {name}")
