@@ -29,7 +29,10 @@ namespace moe {
 
 constexpr int kMaxLocal = 1024;
 // Row caps the panel GEMM chooses from per launch (largest first; all are
-// multiples of 32 and at most the 288 rows a tile holds).
+// multiples of 32 and at most the 288 rows a tile holds). (Caps of 96 and 64
+// rows, which give a down GEMM with few experts and few column panels tiles
+// for every CU, measured no faster: such tiles are bound by the operand bytes
+// one CU fetches per cycle, not by the idle CUs.)
 constexpr int kRowCaps = 6;
 __device__ constexpr int kRowCap[kRowCaps] = {288, 256, 224, 192, 160, 128};
 constexpr int kRowCapMin = 128;
@@ -422,13 +425,17 @@ panel_gemm_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __rest
   __shared__ int s_off[kMaxLocal + 1];
   __shared__ int s_tpre[kMaxLocal + 1];
   __shared__ int s_tmp[dma::kWaves];
-  __shared__ int s_cand[2 * kRowCaps];
+  __shared__ unsigned long long s_ntile[kRowCaps];
+  __shared__ int s_cand[kRowCaps];
   MOE_LDS char* lds = (MOE_LDS char*)smem;
 
   const int ntn = SWIGLU ? (N + kBN / 2 - 1) / (kBN / 2) : (N + kBN - 1) / kBN;
   constexpr int kPerT = (kMaxLocal + dma::kThreads - 1) / dma::kThreads;
   int me[kPerT];
-  if (threadIdx.x < 2 * kRowCaps) s_cand[threadIdx.x] = 0;
+  if (threadIdx.x < kRowCaps) {
+    s_ntile[threadIdx.x] = 0;
+    s_cand[threadIdx.x] = 0;
+  }
 #pragma unroll
   for (int q = 0; q < kPerT; ++q) {
     const int i = threadIdx.x * kPerT + q;
@@ -445,30 +452,35 @@ panel_gemm_kernel(const uint16_t* __restrict__ A, int lda, const int32_t* __rest
   // Row cap of the launch: for each candidate cap, the tile count and the
   // tallest row block; the cap whose estimate ceil(tiles / grid) x (tallest
   // block + 256) is lowest wins (a tile's time grows with its rows plus its
-  // 256 weight columns), the larger cap on ties. Every workgroup gets the same
+  // 256 weight columns), the larger cap on ties. A cap whose tile count does
+  // not fit the 31-bit tile indices is skipped (the host rejects launches
+  // where even the largest cap's does not). Every workgroup gets the same
   // sums and picks the same cap.
 #pragma unroll
   for (int c = 0; c < kRowCaps; ++c) {
-    int tl = 0, hm = 0;
+    unsigned long long tl = 0;
+    int hm = 0;
 #pragma unroll
     for (int q = 0; q < kPerT; ++q) {
       if (me[q] > 0) {
         const int nrt = (me[q] + kRowCap[c] - 1) / kRowCap[c];
-        tl += nrt * ntn;
+        tl += (unsigned long long)nrt * (unsigned long long)ntn;
         hm = max(hm, (((me[q] + nrt - 1) / nrt) + 15) & ~15);
       }
     }
-    if (tl > 0) atomicAdd(&s_cand[c], tl);
-    if (hm > 0) atomicMax(&s_cand[kRowCaps + c], hm);
+    if (tl > 0) atomicAdd(&s_ntile[c], tl);
+    if (hm > 0) atomicMax(&s_cand[c], hm);
   }
   __syncthreads();
   int row_cap = kRowCap[0];
   {
-    int64_t best = -1;
+    unsigned long long best = ~0ull;
 #pragma unroll
     for (int c = 0; c < kRowCaps; ++c) {
-      const int64_t est = int64_t((s_cand[c] + int(gridDim.x) - 1) / int(gridDim.x)) * (s_cand[kRowCaps + c] + kBN);
-      if (best < 0 || est < best) {
+      const unsigned long long tl = s_ntile[c];
+      if (tl >= (1ull << 31)) continue;
+      const unsigned long long est = (tl + gridDim.x - 1) / gridDim.x * (unsigned long long)(s_cand[c] + kBN);
+      if (est < best) {
         best = est;
         row_cap = kRowCap[c];
       }
@@ -598,6 +610,10 @@ hipError_t launch_panel(int64_t tiles, hipStream_t stream, const uint16_t* A, in
     return SWIGLU ? launch_grouped_gemv1(A, lda, gather_src, gather_k, gather_rows, offsets, E_local, capacity, W, K,
                                          N, C, stream)
                   : launch_grouped_gemv2(A, offsets, E_local, capacity, W, N, K, row_info, C, y, stream);
+  // the kernel indexes tiles with 31 bits; at the largest row cap the count
+  // must fit (smaller caps are taken only where theirs fits too)
+  const int64_t ntn = SWIGLU ? ceil_div(N, dma::panel::kBN / 2) : ceil_div(N, dma::panel::kBN);
+  if ((ceil_div(capacity, 288) + E_local) * ntn >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const bool half = K % dma::panel::kSK != 0;
   auto* kern = half ? panel_gemm_kernel<SWIGLU, FUSE, true> : panel_gemm_kernel<SWIGLU, FUSE, false>;
   hipLaunchKernelGGL(kern, dim3(dma_grid(tiles)), dim3(dma::kThreads), 0, stream, A, lda, offsets, E_local, capacity,
