@@ -30,10 +30,13 @@ STAGES = ["route", "dispatch", "gemm1_gate_up_swiglu", "gemm2_down", "combine"]
 # GEMM1 HBM traffic comes from rocprofv3 counter runs summarised (by
 # --summarize-counters) in this file; it is reported only while the kernel
 # sources still hash to what was profiled.
-COUNTERS_MD = os.path.join(ROOT, "profiles", "gemm1_dsr1_ep8_share_counters.md")
+COUNTERS_MD = os.path.join(ROOT, "profiles", "counters_dsr1_ep8_share.md")
 GEMM1_SOURCES = ["expert_token_routing_amd/csrc/expert_ffn.hip", "expert_token_routing_amd/csrc/gemm_dma.h",
                  "expert_token_routing_amd/csrc/gemm_tile.h", "expert_token_routing_amd/csrc/moe_device.h"]
-GEMM1_KERNEL = "panel_gemm_kernel<true, false, false>"
+GEMM1_KERNEL = "moe::panel_gemm_kernel<true, false, false>"
+CALIB_LIB = os.path.join(ROOT, "expert_token_routing_amd", "libmoe_calib.so")
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+DMA_CALIB_KERNEL = "(anonymous namespace)::dma_read_kernel"
 
 
 def log(*a):
@@ -51,10 +54,20 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=16384,
                     help="tokens of the workload the CPU oracle runs on (bounded sample)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="before timing, copy a buffer of this many MiB device to device once (a plain copy of "
-                         "known size that scales hardware byte counters); 0 = off")
-    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COMMAND"),
-                    help="print the markdown summary of two rocprofv3 --pmc output folders and exit")
+                    help="before timing, copy a buffer of this many MiB device to device once and read it once "
+                         "more with the GEMMs' direct-to-LDS loads (libmoe_calib.so): reads and writes of known "
+                         "size that scale hardware byte counters; 0 = off")
+    ap.add_argument("--library-reference", action="store_true",
+                    help="instead of the share, time torch.matmul / torch.bmm (hipBLASLt, bf16) on dense and batched "
+                         "products of the workload's GEMM shapes and print one JSON line")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="print a markdown per-kernel summary of rocprofv3 --pmc output folders (one per counter "
+                         "pass) and exit; see --profile-command")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a markdown table of a rocprofv3 --kernel-trace --stats output folder and exit")
+    ap.add_argument("--profile-command", default="",
+                    help="with --summarize-*: the command(s) that produced the folders, quoted in the summary")
+    ap.add_argument("--profile-title", default="", help="with --summarize-*: the summary's title")
     ap.add_argument("--cold-steps", type=int, default=5,
                     help="extra steps timed with a 1 GiB write between them (evicts L2 / Infinity Cache); 0 = off")
     ap.add_argument("--ep-sweep", default="",
@@ -81,59 +94,200 @@ def recorded_gemm1_traffic():
             kv = dict(line.strip()[2:].split(": ", 1) for line in f if line.startswith("- ") and ": " in line)
     except OSError:
         return None, "no counter summary"
-    if kv.get("source_sha256") != gemm1_sources_sha256():
+    if kv.get("gemm1_source_sha256") != gemm1_sources_sha256():
         return None, "kernel sources changed since the counters were taken"
-    return float(kv["traffic_bytes_per_launch"]), f"rocprofv3 FETCH_SIZE/WRITE_SIZE, {os.path.basename(COUNTERS_MD)}"
+    return (float(kv["gemm1_traffic_bytes_per_launch"]),
+            f"rocprofv3 FETCH_SIZE/WRITE_SIZE, {os.path.relpath(COUNTERS_MD, ROOT)}")
 
 
-def summarize_counters(fetch_dir, write_dir, command):
-    """Markdown summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE)
-    of a bench.py run with --copy-calibration-mib: per-dispatch KiB of the
-    GEMM1 kernel, scaled by what the counters read for the calibration copy."""
+def short_kernel_name(name):
+    """Kernel name without its argument list (and without a leading 'void ')."""
+    name = name.strip()
+    if name.startswith("void "):
+        name = name[5:]
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0 and i > 0:
+            name = name[:i]
+            break
+    if len(name) > 72 and "<" in name:  # library kernels with long template arguments
+        name = name[:name.index("<")] + "<...>"
+    return name
+
+
+def read_counter_dirs(dirs):
+    """Per kernel: per-dispatch durations (ns) and per-dispatch counter
+    values (summed over the rows a dispatch has), from rocprofv3 --pmc csv
+    folders -- one folder per counter pass."""
     import csv
     import glob
+    per = {}
+    for d in dirs:
+        for fn in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            with open(fn) as f:
+                for r in csv.DictReader(f):
+                    key = (fn, int(r["Dispatch_Id"]))
+                    rec = per.setdefault(key, {"kernel": short_kernel_name(r["Kernel_Name"]),
+                                               "dur": int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), "c": {}})
+                    rec["c"][r["Counter_Name"]] = rec["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    kern = {}
+    for rec in per.values():
+        k = kern.setdefault(rec["kernel"], {"dur": [], "c": {}})
+        k["dur"].append(rec["dur"])
+        for c, v in rec["c"].items():
+            k["c"].setdefault(c, []).append(v)
+    return kern
 
-    def per_dispatch(d, counter):
-        out = {}
-        for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-            for r in csv.DictReader(open(fn)):
-                if r["Counter_Name"] != counter:
-                    continue
-                key = int(r["Dispatch_Id"])
-                name, v = r["Kernel_Name"], float(r["Counter_Value"])
-                out[key] = (name, out.get(key, (name, 0.0))[1] + v)
-        return out
 
-    fetch, write = per_dispatch(fetch_dir, "FETCH_SIZE"), per_dispatch(write_dir, "WRITE_SIZE")
-    copy_f = max(v for n, v in fetch.values() if "copyBuffer" in n)
-    copy_w = max(v for n, v in write.values() if "copyBuffer" in n)
+def summarize_counters(dirs, command, title):
+    """Markdown per-kernel summary of rocprofv3 --pmc runs of a bench.py run
+    with --copy-calibration-mib M (the copy and the direct-to-LDS read of M
+    MiB are the byte-counter calibration). Derived figures, per dispatch:
+    engine clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; MFMA busy =
+    SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (GRBM_GUI_ACTIVE / 8);
+    LDS bank-conflict share = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE;
+    HBM bytes = FETCH_SIZE, WRITE_SIZE (KiB) x the calibration scale; read
+    bytes by request size = 32 / 64 / 128 x TCC_EA0_RDREQ_{32B,64B,128B}_sum;
+    L2 hit rate = TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum)."""
     import re
-    mib = int(re.search(r"--copy-calibration-mib (\d+)", command).group(1))
-    f_scale, w_scale = mib * 1024.0 / copy_f, mib * 1024.0 / copy_w
-    g_f = [v for n, v in fetch.values() if GEMM1_KERNEL in n.replace("moe::", "").replace("void ", "")]
-    g_w = [v for n, v in write.values() if GEMM1_KERNEL in n.replace("moe::", "").replace("void ", "")]
-    f_kib, w_kib = sum(g_f) / len(g_f), sum(g_w) / len(g_w)
-    traffic = (f_kib * f_scale + w_kib * w_scale) * 1024.0
-    lines = [
-        "# HBM traffic of the gate/up GEMM (panel_gemm_kernel<true, false, false>), DeepSeek-R1-shaped share",
-        "",
-        "Two counter runs (FETCH_SIZE, then WRITE_SIZE) of the command below; the calibration copy of "
-        f"{mib} MiB device to device reads {copy_f:.0f} KiB as FETCH_SIZE and {copy_w:.0f} KiB as WRITE_SIZE, "
-        "so the counters are scaled by the factors below to bytes.",
-        "",
-        "```",
-        command,
-        "```",
-        "",
-        f"- kernel: {GEMM1_KERNEL}",
-        f"- dispatches: {len(g_f)} (FETCH_SIZE), {len(g_w)} (WRITE_SIZE)",
-        f"- fetch_kib_per_launch: {f_kib:.1f}",
-        f"- write_kib_per_launch: {w_kib:.1f}",
-        f"- fetch_scale: {f_scale:.4f}",
-        f"- write_scale: {w_scale:.4f}",
-        f"- traffic_bytes_per_launch: {traffic:.0f}",
-        f"- source_sha256: {gemm1_sources_sha256()}",
-    ]
+
+    import numpy as np
+    kern = read_counter_dirs(dirs)
+    m = re.search(r"--copy-calibration-mib (\d+)", command)
+    known = int(m.group(1)) << 20 if m else None  # no calibration: no byte scales
+
+    def mean(k, c):
+        v = kern.get(k, {}).get("c", {}).get(c)
+        return float(np.mean(v)) if v else None
+
+    def calib(k, c):  # the largest dispatch of a calibration kernel: the M MiB one
+        v = kern.get(k, {}).get("c", {}).get(c)
+        return max(v) if v else None
+
+    copy_f, copy_w = calib(COPY_KERNEL, "FETCH_SIZE"), calib(COPY_KERNEL, "WRITE_SIZE")
+    dma_f = calib(DMA_CALIB_KERNEL, "FETCH_SIZE")
+    f_scale = known / (copy_f * 1024.0) if (copy_f and known) else None
+    w_scale = known / (copy_w * 1024.0) if (copy_w and known) else None
+    dma_scale = known / (dma_f * 1024.0) if (dma_f and known) else None
+    lines = [f"# {title}" if title else "# Counter summary", "",
+             "rocprofv3 counter passes (one `--pmc` set per run) of the command(s) below, averaged per dispatch "
+             "of each kernel.", "", "```", command, "```", ""]
+    if known:
+        lines += ["## Byte-counter calibration", "",
+                  f"Known sizes: the device-to-device copy reads and writes {known >> 20} MiB "
+                  f"(`{COPY_KERNEL}`); `{DMA_CALIB_KERNEL}` (libmoe_calib.so) reads the same {known >> 20} MiB once "
+                  "with the 16-byte `buffer_load_dwordx4 ... lds` loads the GEMM operand stages use.", "",
+                  "| calibration | counter | reads (KiB) | known (KiB) | scale |", "|---|---|---:|---:|---:|"]
+        for name, c, v, sc in ((COPY_KERNEL, "FETCH_SIZE", copy_f, f_scale),
+                               (COPY_KERNEL, "WRITE_SIZE", copy_w, w_scale),
+                               (DMA_CALIB_KERNEL, "FETCH_SIZE", dma_f, dma_scale)):
+            if v:
+                lines.append(f"| `{name}` | {c} | {v:.0f} | {known / 1024:.0f} | {sc:.4f} |")
+    req = [(COPY_KERNEL, "copy"), (DMA_CALIB_KERNEL, "direct-to-LDS read")]
+    if known and any(calib(k, "TCC_EA0_RDREQ_sum") for k, _ in req):
+        lines += ["", "Read requests the L2 sent to memory, by size (the same calibration dispatches):", "",
+                  "| calibration | requests | 32 B | 64 B | 128 B | bytes by size / known |",
+                  "|---|---:|---:|---:|---:|---:|"]
+        for k, lab in req:
+            tot = calib(k, "TCC_EA0_RDREQ_sum")
+            if not tot:
+                continue
+            r32, r64, r128 = (calib(k, f"TCC_EA0_RDREQ_{b}_sum") or 0.0 for b in ("32B", "64B", "128B"))
+            lines.append(f"| {lab} | {tot:.0f} | {r32:.0f} | {r64:.0f} | {r128:.0f} | "
+                         f"{(32 * r32 + 64 * r64 + 128 * r128) / known:.4f} |")
+    lines += ["", "## Per kernel", "",
+              "| kernel | dispatches | avg (us) | clock (GHz) | MFMA busy | LDS conflict | HBM read (MB) | "
+              "HBM write (MB) | HBM GB/s | read by req. size (MB) | L2 hit |",
+              "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    kv = []
+    order = sorted(kern, key=lambda k: -float(np.mean(kern[k]["dur"])) * len(kern[k]["dur"]))
+    for k in order:
+        if k in (COPY_KERNEL, DMA_CALIB_KERNEL):
+            continue
+        dur = float(np.mean(kern[k]["dur"]))
+        n = min(len(v) for v in kern[k]["c"].values())  # counters taken in one pass only
+        grbm, mf = mean(k, "GRBM_GUI_ACTIVE"), mean(k, "SQ_VALU_MFMA_BUSY_CYCLES")
+        conf, lact = mean(k, "SQ_LDS_BANK_CONFLICT"), mean(k, "SQ_LDS_IDX_ACTIVE")
+        fe, wr = mean(k, "FETCH_SIZE"), mean(k, "WRITE_SIZE")
+        hit, miss = mean(k, "TCC_HIT_sum"), mean(k, "TCC_MISS_sum")
+        rq = [mean(k, f"TCC_EA0_RDREQ_{b}_sum") for b in ("32B", "64B", "128B")]
+        clk = grbm / 8 / dur if (grbm and dur > 20e3) else None  # short launches: fixed overhead dominates
+        busy = mf / 1024 / (grbm / 8) if (mf is not None and grbm) else None
+        rd = fe * 1024 * f_scale if (fe is not None and f_scale) else None
+        wb = wr * 1024 * w_scale if (wr is not None and w_scale) else None
+        gbs = (rd + wb) / dur if (rd is not None and wb is not None) else None
+        by_size = (32 * (rq[0] or 0) + 64 * (rq[1] or 0) + 128 * (rq[2] or 0)) if any(
+            v is not None for v in rq) else None
+
+        def f(v, fmt):
+            return "-" if v is None else format(v, fmt)
+        lines.append(f"| `{k}` | {n} | {dur / 1e3:.1f} | {f(clk, '.2f')} | {f(busy and 100 * busy, '.1f')}"
+                     f"{'%' if busy is not None else ''} | "
+                     f"{f(conf / lact * 100 if (conf is not None and lact) else None, '.2f')}"
+                     f"{'%' if (conf is not None and lact) else ''} | {f(rd and rd / 1e6, '.1f')} | "
+                     f"{f(wb and wb / 1e6, '.1f')} | {f(gbs, '.0f')} | {f(by_size and by_size / 1e6, '.1f')} | "
+                     f"{f(hit / (hit + miss) * 100 if (hit is not None and miss is not None and hit + miss > 0) else None, '.1f')}"
+                     f"{'%' if (hit is not None and miss) else ''} |")
+        if k == GEMM1_KERNEL and rd is not None and wb is not None:
+            kv += [f"- gemm1_traffic_bytes_per_launch: {rd + wb:.0f}",
+                   f"- gemm1_source_sha256: {gemm1_sources_sha256()}"]
+    lines += ["", "HBM bytes use the copy's scales (read and write). MFMA busy and clock need GRBM_GUI_ACTIVE and "
+              "SQ_VALU_MFMA_BUSY_CYCLES in the same pass; a '-' is a counter not collected.", ""]
+    # the load path of the kernels that move most data, when its counters were taken
+    mem = [k for k in order if mean(k, "TD_TD_BUSY_sum") is not None and mean(k, "TCP_TCC_READ_REQ_sum")
+           and float(np.mean(kern[k]["dur"])) > 20e3 and k not in (COPY_KERNEL,)]
+    if mem:
+        lines += ["## Load path", "",
+                  "Per dispatch; busy and stall shares are of the dispatch's cycles on each of the 256 CUs "
+                  "(counter sum / 256 / (GRBM_GUI_ACTIVE / 8)). L2 latency = TCP_TCC_READ_REQ_LATENCY_sum / "
+                  "TCP_TCC_READ_REQ_sum (cycles per L1-to-L2 read request); lines in flight per CU = requests x "
+                  "latency / 256 / cycles (Little's law).", "",
+                  "| kernel | L1->L2 reads | L2 hit | L2 latency (cyc) | lines in flight / CU | TA busy | "
+                  "TD busy | TD waiting on L1 | L1 waiting on L2 |",
+                  "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+        for k in mem:
+            grbm = mean(k, "GRBM_GUI_ACTIVE")
+            cyc = grbm / 8 if grbm else None
+            req, lat = mean(k, "TCP_TCC_READ_REQ_sum"), mean(k, "TCP_TCC_READ_REQ_LATENCY_sum")
+            hit, miss = mean(k, "TCC_HIT_sum"), mean(k, "TCC_MISS_sum")
+
+            def share(c):
+                v = mean(k, c)
+                return "-" if (v is None or not cyc) else f"{100 * v / 256 / cyc:.0f}%"
+            lat_c = lat / req if (lat and req) else None
+            fl = req * lat_c / 256 / cyc if (lat_c and cyc) else None
+            lines.append(f"| `{k}` | {req:.3g} | "
+                         f"{'-' if hit is None or miss is None else f'{100 * hit / (hit + miss):.0f}%'} | "
+                         f"{'-' if lat_c is None else f'{lat_c:.0f}'} | {'-' if fl is None else f'{fl:.0f}'} | "
+                         f"{share('TA_TA_BUSY_sum')} | {share('TD_TD_BUSY_sum')} | {share('TD_TC_STALL_sum')} | "
+                         f"{share('TCP_PENDING_STALL_CYCLES_sum')} |")
+        lines.append("")
+    if kv:
+        lines += ["Recorded for bench.py's roofline (the gate/up GEMM's HBM bytes per launch and the hash of its "
+                  "sources when they were taken):", ""] + kv
+    return "\n".join(lines) + "\n"
+
+
+def summarize_trace(d, command, title):
+    """Markdown table of a rocprofv3 --kernel-trace --stats folder."""
+    import csv
+    import glob
+    rows = []
+    for fn in glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True):
+        with open(fn) as f:
+            rows += list(csv.DictReader(f))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    tot = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = [f"# {title}" if title else "# Kernel trace", "", "```", command, "```", "",
+             "| kernel | calls | avg (us) | min (us) | max (us) | share |", "|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        lines.append(f"| `{short_kernel_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{100 * float(r['TotalDurationNs']) / tot:.1f}% |")
     return "\n".join(lines) + "\n"
 
 
@@ -155,6 +309,106 @@ def algorithmic(cfg, N, U, E_hit, fused_gather=True):
         "combine": dict(bytes=2.0 * N * H + 2.0 * T * H + 8.0 * T * k),
         "dispatch_rows": rows,
     }
+
+
+def calib_lib():
+    """libmoe_calib.so (include/moe_calib.h), built beside libmoe.so."""
+    import ctypes
+    if not os.path.exists(CALIB_LIB):
+        sys.exit(f"{CALIB_LIB} is missing: build with python -m expert_token_routing_amd.build_lib")
+    cal = ctypes.CDLL(CALIB_LIB)
+    cal.moe_calib_dma_read.restype = ctypes.c_int
+    cal.moe_calib_dma_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    cal.moe_calib_mfma_loop.restype = ctypes.c_int
+    cal.moe_calib_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double),
+                                        ctypes.c_void_p]
+    return cal
+
+
+def mfma_attainable(stream, dev):
+    """bf16 matrix-core rate of the register-only MFMA loop (no memory
+    traffic), 2 and 1 waves per SIMD, best of 5 launches each (TFLOP/s)."""
+    import ctypes
+
+    import torch
+    cal = calib_lib()
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    out = {}
+    for wps, iters in ((2, 16000), (1, 32000)):
+        flop = ctypes.c_double(0)
+        best = None
+        for _ in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            st = cal.moe_calib_mfma_loop(iters, wps, ctypes.c_void_p(sink.data_ptr()), ctypes.byref(flop),
+                                         ctypes.c_void_p(stream.cuda_stream))
+            e1.record(stream)
+            if st != 0:
+                sys.exit(f"moe_calib_mfma_loop failed with status {st}")
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            if best is None or ms < best:
+                best = ms
+        out[f"tflops_{wps}_waves_per_simd"] = round(flop.value / (best * 1e-3) / 1e12, 1)
+    return out
+
+
+def library_reference(args):
+    """hipBLASLt (through torch.matmul / torch.bmm, bf16, float32 accumulate)
+    on the workload's GEMM shapes: the dense products over all T tokens with
+    one weight matrix, the batched products with E_local weight matrices of
+    the mean rows per expert, and a square 8192 product. Context for what
+    the vendor library reaches on this chip; nothing here is the share."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    cfg = W.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    rows = (cfg.T * cfg.k * cfg.E_local) // cfg.E  # expected rows of the share
+    per = max(1, rows // cfg.E_local)
+
+    def rnd(*shape):
+        return (torch.randn(*shape, device=dev, generator=g, dtype=torch.float32) * 0.05).to(torch.bfloat16)
+
+    cases = [
+        (f"dense [{cfg.T} x {cfg.H}] @ [{cfg.H} x {2 * cfg.I}]", lambda: (rnd(cfg.T, cfg.H), rnd(cfg.H, 2 * cfg.I)),
+         torch.matmul, 2.0 * cfg.T * cfg.H * 2 * cfg.I),
+        (f"dense [{cfg.T} x {cfg.I}] @ [{cfg.I} x {cfg.H}]", lambda: (rnd(cfg.T, cfg.I), rnd(cfg.I, cfg.H)),
+         torch.matmul, 2.0 * cfg.T * cfg.I * cfg.H),
+        (f"batched {cfg.E_local} x [{per} x {cfg.H}] @ [{cfg.H} x {2 * cfg.I}]",
+         lambda: (rnd(cfg.E_local, per, cfg.H), rnd(cfg.E_local, cfg.H, 2 * cfg.I)), torch.bmm,
+         2.0 * cfg.E_local * per * cfg.H * 2 * cfg.I),
+        (f"batched {cfg.E_local} x [{per} x {cfg.I}] @ [{cfg.I} x {cfg.H}]",
+         lambda: (rnd(cfg.E_local, per, cfg.I), rnd(cfg.E_local, cfg.I, cfg.H)), torch.bmm,
+         2.0 * cfg.E_local * per * cfg.I * cfg.H),
+        ("dense [8192 x 8192] @ [8192 x 8192]", lambda: (rnd(8192, 8192), rnd(8192, 8192)), torch.matmul,
+         2.0 * 8192 ** 3),
+    ]
+    stream = torch.cuda.current_stream(dev)
+    res = []
+    for name, make, fn, flop in cases:
+        a, b = make()  # both operands contiguous
+        for _ in range(3):
+            fn(a, b)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(11)]
+        evs[0].record(stream)
+        for i in range(10):
+            fn(a, b)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([evs[i].elapsed_time(evs[i + 1]) for i in range(10)]))
+        tf = flop / (ms * 1e-3) / 1e12
+        res.append({"case": name, "us": round(ms * 1e3, 1), "tflops": round(tf, 1),
+                    "frac_mfma_bf16": round(tf / PEAK_BF16_TFLOPS, 4)})
+        log(f"[libref] {name}: {ms * 1e3:.1f} us, {tf:.0f} TFLOP/s")
+        del a, b
+    print(json.dumps({"metric": "vendor library (hipBLASLt via torch, bf16) on the workload's GEMM shapes",
+                      "workload": cfg.name, "mfma_attainable": mfma_attainable(stream, dev), "cases": res,
+                      "torch": torch.__version__}), flush=True)
 
 
 def cpu_baseline(inp, sample_tokens):
@@ -291,7 +545,10 @@ def ep_sweep(args):
 def main():
     args = parse()
     if args.summarize_counters:
-        print(summarize_counters(*args.summarize_counters), end="")
+        print(summarize_counters(args.summarize_counters, args.profile_command, args.profile_title), end="")
+        return
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.profile_command, args.profile_title), end="")
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -300,6 +557,9 @@ def main():
         sys.exit(2)
     if args.ep_sweep:
         ep_sweep(args)
+        return
+    if args.library_reference:
+        library_reference(args)
         return
 
     import numpy as np
@@ -345,6 +605,13 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: {nb} bytes read, {nb} bytes written")
+        import ctypes
+        cal = calib_lib()
+        st = cal.moe_calib_dma_read(ctypes.c_void_p(src.data_ptr()), nb, ctypes.c_void_p(stream.cuda_stream))
+        if st != 0:
+            sys.exit(f"moe_calib_dma_read failed with status {st}")
+        torch.cuda.synchronize()
+        log(f"[bench] direct-to-LDS read calibration: {nb} bytes read")
         del src, dst
 
     log(f"[bench] warmup {args.warmup}")
@@ -501,9 +768,34 @@ def main():
         roofline = {"bound": "hbm", "kernel": "grouped GEMM1 (gate/up + SwiGLU)",
                     "achieved": round(g1_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(g1_gbs / PEAK_HBM_GBS, 4)}
+    # the matrix-core rate this chip sustains (register-only MFMA loop), as
+    # context for the spec peak the fractions use
+    attain = mfma_attainable(stream, dev)
+    att = attain["tflops_2_waves_per_simd"]
+    log(f"[bench] register-only MFMA loop: {attain}")
     roofline.update({"traffic": traffic, "traffic_unit": "HBM bytes per launch", "traffic_source": traffic_note,
                      "intensity_flop_per_byte": round(intensity, 1), "ridge_flop_per_byte": round(ridge, 1),
-                     "algorithmic_bytes": w1["bytes"], "algorithmic_flop": w1["flop"]})
+                     "algorithmic_bytes": w1["bytes"], "algorithmic_flop": w1["flop"],
+                     "attainable_peak": att, "frac_of_attainable": round(g1 / att, 4)})
+    # the router: logits as three bf16 products (the float32 weight split into
+    # three bf16 planes, exact), so 3 x 2 T E H matrix-core flop, then top-k
+    # over the float32 logits (and the partial sums of a split k range)
+    r_flop = 3 * 2.0 * cfg.T * cfg.E * cfg.H
+    r_us = float(stage_avg[0]) * 1e3
+    r_tf = r_flop / (r_us * 1e-6) / 1e12
+    # top-k reads the logits and one partial sum and writes the logits back
+    # (12 T E bytes) and the selection (8 T k); the split reads the float32
+    # weight and writes three bf16 planes (10 E H). The logits kernel's own
+    # loads and stores overlap its matrix work.
+    topk_bytes = 12.0 * cfg.T * cfg.E + 8.0 * cfg.T * cfg.k
+    split_bytes = 10.0 * cfg.E * cfg.H
+    floor_us = (r_flop / (att * 1e12) + (topk_bytes + split_bytes) / (PEAK_HBM_GBS * 1e9)) * 1e6
+    route_roofline = {"bound": "mfma", "kernel": "route: bf16x3 split logits, then top-k",
+                      "mfma_flop": r_flop, "achieved": round(r_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(r_tf / PEAK_BF16_TFLOPS, 4), "frac_of_attainable": round(r_tf / att, 4),
+                      "floor_us": round(floor_us, 1),
+                      "floor_note": "three bf16 products at the attainable MFMA rate, plus the split's and the "
+                                    "top-k's bytes at the HBM peak"}
     gemm_ms = stage_avg[2] + stage_avg[3]
     gemm_tflops = 6.0 * N * cfg.H * cfg.I / (gemm_ms * 1e-3) / 1e12
     ms_per_step = wall / args.steps * 1e3
@@ -525,7 +817,10 @@ def main():
                    "e0": cfg.e0, "E_local": cfg.E_local, "renormalize": cfg.renormalize,
                    "parallelism": "one EP rank's share on 1 GPU"},
         "roofline": roofline,
-        "grouped_gemm": {"tflops": round(gemm_tflops, 2), "frac_mfma_bf16": round(gemm_tflops / PEAK_BF16_TFLOPS, 4)},
+        "grouped_gemm": {"tflops": round(gemm_tflops, 2), "frac_mfma_bf16": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+                         "frac_of_attainable": round(gemm_tflops / att, 4)},
+        "route_roofline": route_roofline,
+        "mfma_attainable": dict(attain, note="register-only v_mfma_f32_16x16x32_bf16 loop, libmoe_calib.so"),
         "stages": stages,
         "dispatch_rows": dispatch_rows,
         "combine_f32": combine_f32,

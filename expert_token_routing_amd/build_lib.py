@@ -2,7 +2,8 @@
 
 Usage: ``python -m expert_token_routing_amd.build_lib`` (or ``build()``).
 Compiles every ``csrc/*.hip`` with hipcc in parallel and links one shared
-library next to this file. Always recompiles.
+library next to this file; ``calib/*.hip`` (counter calibration,
+include/moe_calib.h) becomes ``libmoe_calib.so`` beside it. Always recompiles.
 """
 from __future__ import annotations
 
@@ -18,6 +19,7 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 BUILD = ROOT / "_build"
 LIB = PKG / "libmoe.so"
+CALIB_LIB = PKG / "libmoe_calib.so"
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 COMMON_FLAGS = [
@@ -52,7 +54,9 @@ def build(verbose: bool = False, jobs: int | None = None) -> pathlib.Path:
     cc = hipcc()
     BUILD.mkdir(exist_ok=True)
     sources = sorted(CSRC.glob("*.hip"))
+    calib = sorted((PKG / "calib").glob("*.hip"))
     objs = [BUILD / (s.stem + ".o") for s in sources]
+    calib_objs = [BUILD / ("calib_" + s.stem + ".o") for s in calib]
 
     def compile_one(pair):
         src, obj = pair
@@ -61,12 +65,13 @@ def build(verbose: bool = False, jobs: int | None = None) -> pathlib.Path:
             print(out)
         return obj
 
-    jobs = jobs or min(len(sources), max(1, min(16, os.cpu_count() or 1)))
+    jobs = jobs or min(len(sources) + len(calib), max(1, min(16, os.cpu_count() or 1)))
     with ThreadPoolExecutor(jobs) as ex:
-        list(ex.map(compile_one, zip(sources, objs)))
-    tmp = LIB.with_suffix(".so.tmp")
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *map(str, objs)])
-    os.replace(tmp, LIB)
+        list(ex.map(compile_one, zip(sources + calib, objs + calib_objs)))
+    for lib, lib_objs in ((LIB, objs), (CALIB_LIB, calib_objs)):
+        tmp = lib.with_suffix(".so.tmp")
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *map(str, lib_objs)])
+        os.replace(tmp, lib)
     if verbose:
         print(f"built {LIB}")
     return LIB

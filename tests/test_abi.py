@@ -12,12 +12,14 @@ import expert_token_routing_amd as M
 from expert_token_routing_amd import _binding as B
 
 HEADER = pathlib.Path(__file__).resolve().parent.parent / "include" / "moe.h"
+CALIB_HEADER = HEADER.with_name("moe_calib.h")
+CALIB_LIB = pathlib.Path(M.__file__).resolve().parent / "libmoe_calib.so"
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below is rejected first
 FAKE_ODD = ctypes.c_void_p(0x10002)  # not 16-byte aligned
 
 
-def header_functions():
-    text = HEADER.read_text()
+def header_functions(header=HEADER):
+    text = header.read_text()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(moe_[a-z_0-9]+)\s*\(", text, flags=re.M)))
 
@@ -29,6 +31,28 @@ def test_library_exports_every_header_symbol():
     for n in names:
         assert hasattr(L, n), f"libmoe.so lacks {n}"
     assert set(names) == set(B.SIGNATURES), (set(names) ^ set(B.SIGNATURES))
+
+
+def test_calibration_library_exports_and_host_checks():
+    """libmoe_calib.so (the counter-calibration read) exports exactly what
+    include/moe_calib.h declares and rejects bad sizes and pointers on the
+    host; bytes = 0 launches nothing."""
+    names = header_functions(CALIB_HEADER)
+    assert names == ["moe_calib_dma_read", "moe_calib_mfma_loop"]
+    L = ctypes.CDLL(str(CALIB_LIB))
+    for n in names:
+        assert hasattr(L, n), n
+    f = L.moe_calib_dma_read
+    f.restype, f.argtypes = ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert f(FAKE, 0, None) == M.MOE_OK
+    for ptr, nbytes in ((FAKE, 1000), (FAKE, 1024 + 16), (FAKE_ODD, 1024), (None, 1024), (FAKE, (1 << 30) + 1024)):
+        assert f(ptr, nbytes, None) == M.MOE_ERR_INVALID_ARG, (ptr, nbytes)
+    g = L.moe_calib_mfma_loop
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    flop = ctypes.c_double(0)
+    for iters, wps, sink in ((0, 2, FAKE), (10, 0, FAKE), (10, 9, FAKE), (10, 2, None)):
+        assert g(iters, wps, sink, ctypes.byref(flop), None) == M.MOE_ERR_INVALID_ARG
 
 
 def test_status_strings():
