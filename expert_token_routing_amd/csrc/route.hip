@@ -362,6 +362,126 @@ route_topk_kernel(float* __restrict__ logits, const float* __restrict__ part, in
 // ---------------------------------------------------------------------------
 // Host-side launchers
 // ---------------------------------------------------------------------------
+// Top-k for E = 64 Q experts (Q = 1, 2, 4, 8, 16; logits 16-byte aligned):
+// lane l holds the Q consecutive experts Q l .. Q l + Q - 1, so every row
+// moves with one or a few vector loads per lane and no per-lane bounds
+// checks. Same arithmetic and the same choices
+// as route_topk_kernel: the k-range parts are added in part order, then the
+// bias; each round takes the largest live logit, the lowest expert id among
+// equal ones (the lowest lane holding it, then its lowest slot); weights are
+// the softmax over all E (or over the k taken, renormalised). Four tokens per
+// workgroup, one per wave.
+template <int Q>
+__device__ __forceinline__ void load_q(const float* __restrict__ p, float (&v)[Q]) {
+  if constexpr (Q % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < Q / 4; ++i) {
+      const float4 f = reinterpret_cast<const float4*>(p)[i];
+      v[4 * i] = f.x;
+      v[4 * i + 1] = f.y;
+      v[4 * i + 2] = f.z;
+      v[4 * i + 3] = f.w;
+    }
+  } else if constexpr (Q == 2) {
+    const float2 f = *reinterpret_cast<const float2*>(p);
+    v[0] = f.x;
+    v[1] = f.y;
+  } else {
+    v[0] = p[0];
+  }
+}
+template <int Q>
+__device__ __forceinline__ void store_q(float* __restrict__ p, const float (&v)[Q]) {
+  if constexpr (Q % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < Q / 4; ++i)
+      reinterpret_cast<float4*>(p)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+  } else if constexpr (Q == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  } else {
+    p[0] = v[0];
+  }
+}
+
+template <int Q>
+__global__ void __launch_bounds__(kThreads)
+route_topk_vec_kernel(float* __restrict__ logits, const float* __restrict__ part, int nparts,
+                      const float* __restrict__ bias, int T, int k, int renormalize, int32_t* __restrict__ topk_idx,
+                      float* __restrict__ topk_w) {
+  constexpr int E = 64 * Q;
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float* row = logits + int64_t(t) * E + Q * lane;
+  float v[Q];
+  load_q<Q>(row, v);
+  if (part != nullptr) {  // logits hold the first k part: add the others in order, then the bias; store the sum
+    const float* prow = part + int64_t(t) * E + Q * lane;
+    const int64_t pstride = int64_t(T) * E;
+    // four parts' loads in flight at a time, added in part order
+    for (int z0 = 0; z0 < nparts; z0 += 4) {
+      float pv[4][Q];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (z0 + u < nparts) load_q<Q>(prow + (z0 + u) * pstride, pv[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (z0 + u < nparts)
+#pragma unroll
+          for (int i = 0; i < Q; ++i) v[i] += pv[u][i];
+    }
+    if (bias != nullptr)  // the bias may sit at any float address: scalar loads
+#pragma unroll
+      for (int i = 0; i < Q; ++i) v[i] += bias[Q * lane + i];
+    store_q<Q>(row, v);
+  }
+  float lm = v[0];
+#pragma unroll
+  for (int i = 1; i < Q; ++i) lm = fmaxf(lm, v[i]);
+  const float m = wave_max_dpp(lm);
+
+  float den_all = 0.f;
+  if (!renormalize) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < Q; ++i) s += expf(v[i] - m);
+    den_all = wave_sum(s);
+  }
+
+  uint32_t live = (Q == 32 ? ~0u : ((1u << Q) - 1u));  // bit i: expert Q lane + i not taken yet
+  int my_e = 0;
+  float my_v = 0.f;
+  for (int j = 0; j < k; ++j) {
+    float cm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < Q; ++i)
+      if ((live >> i) & 1u) cm = fmaxf(cm, v[i]);
+    const float bv = wave_max_dpp(cm);
+    int fi = Q;  // this lane's lowest live slot holding the maximum
+#pragma unroll
+    for (int i = Q - 1; i >= 0; --i)
+      if (((live >> i) & 1u) && v[i] == bv) fi = i;
+    const uint64_t hit = ballot(fi < Q);
+    const int bl = __ffsll((unsigned long long)hit) - 1;
+    const int bi = __builtin_amdgcn_readlane(fi, bl);
+    if (lane == bl) live &= ~(1u << bi);
+    if (lane == j) {
+      my_e = Q * bl + bi;
+      my_v = bv;
+    }
+  }
+  const float p = lane < k ? expf(my_v - m) : 0.f;
+  float den = den_all;
+  if (renormalize) {
+    den = 0.f;
+    for (int j = 0; j < k; ++j) den += shfl(p, j);
+  }
+  if (lane < k) {
+    topk_idx[int64_t(t) * k + lane] = my_e;
+    topk_w[int64_t(t) * k + lane] = p / den;
+  }
+}
+
 int route_k_parts(int T, int H, int E) {
   if (H % routedma::kSK != 0) return 1;
   const int nk_all = H / routedma::kSK;
@@ -413,6 +533,26 @@ hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b
     const float* pt = split ? part : nullptr;
     dim3 grid(unsigned((T + 3) / 4));
     const int epl = (E + 63) / 64;
+#define MOE_TOPK_VEC(Q)                                                                                          \
+  hipLaunchKernelGGL(route_topk_vec_kernel<Q>, grid, dim3(kThreads), 0, stream, logits, pt, parts - 1, bias, T, k, \
+                     renormalize, topk_idx, topk_w)
+    // the vector loads and stores need 16-byte aligned rows (the partial
+    // sums live in the workspace, which is)
+    if (E % 64 == 0 && (epl == 1 || epl == 2 || epl == 4 || epl == 8 || epl == 16) &&
+        (reinterpret_cast<uintptr_t>(logits) & 15u) == 0) {
+      if (epl == 1)
+        MOE_TOPK_VEC(1);
+      else if (epl == 2)
+        MOE_TOPK_VEC(2);
+      else if (epl == 4)
+        MOE_TOPK_VEC(4);
+      else if (epl == 8)
+        MOE_TOPK_VEC(8);
+      else
+        MOE_TOPK_VEC(16);
+      return hipGetLastError();
+    }
+#undef MOE_TOPK_VEC
 #define MOE_TOPK_LAUNCH(EPL)                                                                                       \
   hipLaunchKernelGGL(route_topk_kernel<EPL>, grid, dim3(kThreads), 0, stream, logits, pt, parts - 1, bias, T, E, k, \
                      renormalize, topk_idx, topk_w)
