@@ -83,15 +83,21 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int64_t bytes) {
 // lds_base + 16 * lane. Written as inline assembly so the compiler does not
 // treat the in-flight transfer as a pending LDS write (it would otherwise wait
 // for all of them before any LDS read); completion is awaited explicitly with
-// s_waitcnt vmcnt. No register is written by the instruction; M0 (the LDS
-// base) is an input the compiler sets.
+// s_waitcnt vmcnt. M0 (the LDS base) is an input the compiler sets.
+// The compiler does not look inside the assembly for hazards: a memory
+// instruction that reads an SGPR written by a vector instruction (the
+// compiler may produce the scalar offset with v_readlane when it keeps
+// scalars in vector-register lanes) needs 5 wait states, else it may use the
+// old value. So the offset is first copied by a scalar move, whose result
+// needs none; the move also gives the wait state after the M0 write. (The
+// build scans the generated code for such a write to the descriptor.)
 __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t voff, uint32_t soff, const MOE_LDS char* lds_base) {
   const uint32_t lds_addr = uint32_t(reinterpret_cast<uintptr_t>(lds_base));
   // keep the scalar offset in an SGPR (soffset takes no literal constants)
   asm volatile("" : "+s"(soff));
-  // one wait state between the M0 write and the LDS-direct load
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :
+  uint32_t s;
+  asm volatile("s_mov_b32 %0, %3\n\tbuffer_load_dwordx4 %1, %2, %0 offen lds"
+               : "=&s"(s)
                : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr)
                : "memory");
 }
