@@ -254,6 +254,185 @@ route_logits_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
   }
 }
 
+// The same product with the float32 weight rows staged as they are (4
+// bytes per value, instead of 6 for the three bf16 planes) and cut into
+// hi + mid + lo in registers, by the same exact steps as route_split_kernel,
+// just before the matrix-core products: the bf16 operands, the products and
+// their order are those of route_logits_dma_kernel, so are the logits, bit
+// for bit. A stage is 32 KiB of token rows and 32 KiB of weight rows (256
+// bytes of one expert's row per stage; 16-byte chunk c of row r sits at
+// chunk position c ^ (r & 15), so the 16 rows a 16-lane read takes hit 16
+// different 16-byte slots).
+constexpr int kWStage = kBN * kSK * 4;                             // 32 KiB of float32 weight rows
+constexpr int kStageW = kAStage + kWStage;                         // 64 KiB
+
+// ROWS float32 rows x 64 k of a k-contiguous matrix: load i of wave w fills
+// rows 4 (i * 8 + w) .. +3, 16 lanes (16 bytes each) per row.
+template <int ROWS>
+struct RowLoaderF32 {
+  static constexpr int kPer = ROWS / 4 / dma::kWaves;
+  dma::i32x4 rsrc;
+  uint32_t voff[kPer];
+  __device__ __forceinline__ void init(const float* tile_base, int ld, int rows) {
+    rsrc = dma::buffer_rsrc(tile_base, int64_t(rows) * ld * 4);
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int r = 4 * (i * dma::kWaves + w) + (lane >> 4);
+      const int c = (lane & 15) ^ (r & 15);
+      voff[i] = uint32_t(min(r, rows - 1)) * uint32_t(ld) * 4u + 16u * uint32_t(c);
+    }
+  }
+  __device__ __forceinline__ void issue(MOE_LDS char* dst, int k0) const {
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) dma::dma16(rsrc, voff[i], 4u * uint32_t(k0), dst + 1024 * (i * dma::kWaves + w));
+  }
+};
+
+// 8 float32 values (two chunks) -> their hi, mid and lo bf16 parts, packed
+// as MFMA operands (value 2 d in the low half of dword d).
+__device__ __forceinline__ void split3(const u32x4& c0, const u32x4& c1, u32x4& hi, u32x4& mid, u32x4& lo) {
+  uint32_t x[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  uint32_t h[8], m[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = x[e] & 0xFFFF0000u;
+    const float r1 = __uint_as_float(x[e]) - __uint_as_float(h[e]);
+    m[e] = __float_as_uint(r1) & 0xFFFF0000u;
+    const float r2 = r1 - __uint_as_float(m[e]);
+    l[e] = __float_as_uint(r2);
+  }
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    // high halves of values 2 d (low half of the dword) and 2 d + 1
+    hi[d] = __builtin_amdgcn_perm(h[2 * d + 1], h[2 * d], 0x07060302u);
+    mid[d] = __builtin_amdgcn_perm(m[2 * d + 1], m[2 * d], 0x07060302u);
+    lo[d] = __builtin_amdgcn_perm(l[2 * d + 1], l[2 * d], 0x07060302u);
+  }
+}
+
+__global__ void __launch_bounds__(dma::kThreads)
+route_logits_w32_kernel(const uint16_t* __restrict__ x, const float* __restrict__ w_router, float* __restrict__ out0,
+                        float* __restrict__ out1, int T, int H, int E, int per) {
+  using namespace dma;
+  __shared__ __attribute__((aligned(1024))) char smem[kBufs * kStageW];
+  MOE_LDS char* lds = (MOE_LDS char*)smem;
+  const int t0 = blockIdx.x * kBM;
+  const int n0 = blockIdx.y * kBN;
+  const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int lane = lane_id();
+  const int nk_all = H / kSK;
+  const int s0 = blockIdx.z * per;
+  const int nk = max(0, min(nk_all, s0 + per) - s0);  // stages of this part
+  float* __restrict__ out = blockIdx.z == 0 ? out0 : out1 + int64_t(blockIdx.z - 1) * T * E;
+
+  RowLoader64<kBM> la;
+  RowLoaderF32<kBN> lb;
+  la.init(x + int64_t(t0) * H, H, min(kBM, T - t0));
+  lb.init(w_router + int64_t(n0) * H, H, min(kBN, E - n0));
+  auto issue = [&](int st) {
+    if (st < nk) {
+      MOE_LDS char* dst = lds + (st % kBufs) * kStageW;
+      la.issue(dst, (s0 + st) * kSK);
+      lb.issue(dst + kAStage, (s0 + st) * kSK);
+    }
+  };
+  // fragment offsets of 16-deep step ks (0..3): A rows wm*64 + fm*32 + lane%32,
+  // chunk 2 ks + lane/32 (swizzled as RowLoader64); weight rows wn*64 +
+  // fn*32 + lane%32, float32 chunks 4 ks + 2 (lane/32) and +1 (swizzled as
+  // RowLoaderF32; the row bits the swizzle uses are those of lane%32)
+  const int khalf = lane >> 5;
+  const int ma = wm * 64 + (lane & 31);
+  const int mb = wn * 64 + (lane & 31);
+  uint32_t aoff[kSK / 16], woff[kSK / 16][2];
+#pragma unroll
+  for (int ks = 0; ks < kSK / 16; ++ks) {
+    aoff[ks] = uint32_t(ma * 128 + 16 * ((2 * ks + khalf) ^ ((ma >> 1) & 7)));
+#pragma unroll
+    for (int e = 0; e < 2; ++e) woff[ks][e] = uint32_t(mb * 256 + 16 * ((4 * ks + 2 * khalf + e) ^ (mb & 15)));
+  }
+  struct F {
+    u32x4 a[kFM];
+    u32x4 wv[kFN][2];
+  };
+  auto load = [&](const MOE_LDS char* st, int ks, F& f) {
+#pragma unroll
+    for (int fm = 0; fm < kFM; ++fm)
+      f.a[fm] = *reinterpret_cast<const MOE_LDS u32x4*>(st + aoff[ks] + fm * 32 * 128);
+#pragma unroll
+    for (int fn = 0; fn < kFN; ++fn)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        f.wv[fn][e] = *reinterpret_cast<const MOE_LDS u32x4*>(st + kAStage + woff[ks][e] + fn * 32 * 256);
+  };
+  f32x16 acc[kFM][kFN];
+#pragma unroll
+  for (int fm = 0; fm < kFM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < kFN; ++fn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
+  auto mma = [&](const F& f) {
+    u32x4 b[kPlanes][kFN];
+#pragma unroll
+    for (int fn = 0; fn < kFN; ++fn) split3(f.wv[fn][0], f.wv[fn][1], b[0][fn], b[1][fn], b[2][fn]);
+#pragma unroll
+    for (int p = 0; p < kPlanes; ++p)
+#pragma unroll
+      for (int fm = 0; fm < kFM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < kFN; ++fn) acc[fm][fn] = mfma32x32x16(f.a[fm], b[p][fn], acc[fm][fn]);
+  };
+  constexpr int kLoads = RowLoader64<kBM>::kPer + RowLoaderF32<kBN>::kPer;  // DMA instructions per wave per stage
+
+  if (nk > 0) {
+    issue(0);
+    issue(1);
+    if (nk > 1)
+      wait_vm_barrier<kLoads>();
+    else
+      wait_vm_barrier<0>();
+    F f0, f1;
+    load(lds, 0, f0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const MOE_LDS char* cur = lds + (kt % kBufs) * kStageW;
+      // steps 0..2: each step's MFMAs cover the next step's LDS reads
+      load(cur, 1, f1);
+      mma(f0);
+      __builtin_amdgcn_sched_barrier(0);
+      load(cur, 2, f0);
+      mma(f1);
+      __builtin_amdgcn_sched_barrier(0);
+      load(cur, 3, f1);
+      mma(f0);
+      __builtin_amdgcn_sched_barrier(0);
+      // step 3: every wave is done reading stage kt and stage kt+1 (the only
+      // one in flight) landed; refill this buffer with stage kt+2
+      wait_lgkm0();
+      wait_vm_barrier<0>();
+      issue(kt + 2);
+      load(lds + ((kt + 1) % kBufs) * kStageW, 0, f0);  // stage nk: a finished buffer, values unused
+      mma(f1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_lgkm0();
+  }
+
+#pragma unroll
+  for (int fn = 0; fn < kFN; ++fn) {
+    const int e = n0 + mb + fn * 32;
+#pragma unroll
+    for (int fm = 0; fm < kFM; ++fm)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int t = t0 + wm * 64 + fm * 32 + mfma_c_row(v, lane);
+        if (t < T && e < E) out[int64_t(t) * E + e] = acc[fm][fn][v];
+      }
+  }
+}
+
 }  // namespace routedma
 
 // One wave per token: top-k by (logit descending, expert id ascending), then
@@ -505,23 +684,32 @@ hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b
                         int renormalize, float* logits, int32_t* topk_idx, float* topk_w, uint16_t* planes, float* part,
                         hipStream_t stream) {
   const int64_t n = int64_t(E) * H;
-  {
+  const int parts = route_k_parts(T, H, E);
+  const bool split = parts > 1;
+  // Cutting the float32 weights in registers is repeated by every token tile:
+  // it pays (no plane pass, a third less weight traffic) for a few tiles and
+  // loses beyond (measured: ahead at 1 and 8 tiles of 256 tokens, behind at
+  // 32 and 64)
+  const bool w32 = split && (T + routedma::kBM - 1) / routedma::kBM <= 8;
+  if (!w32) {
     const int threads = 256;
     const int64_t blocks = std::min<int64_t>((n / 4 + threads - 1) / threads, 4096);
     hipLaunchKernelGGL(route_split_kernel, dim3(unsigned(blocks)), dim3(threads), 0, stream, w_router, planes, n);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  const int parts = route_k_parts(T, H, E);
-  const bool split = parts > 1;
   {
     if (split) {
       const int nk_all = H / routedma::kSK;
       const int per = (nk_all + parts - 1) / parts;
       dim3 grid(unsigned((T + routedma::kBM - 1) / routedma::kBM), unsigned((E + routedma::kBN - 1) / routedma::kBN),
                 unsigned(parts));
-      hipLaunchKernelGGL(routedma::route_logits_dma_kernel, grid, dim3(dma::kThreads), 0, stream, x, planes, logits,
-                         part, T, H, E, per);
+      if (w32)
+        hipLaunchKernelGGL(routedma::route_logits_w32_kernel, grid, dim3(dma::kThreads), 0, stream, x, w_router,
+                           logits, part, T, H, E, per);
+      else
+        hipLaunchKernelGGL(routedma::route_logits_dma_kernel, grid, dim3(dma::kThreads), 0, stream, x, planes, logits,
+                           part, T, H, E, per);
     } else {
       dim3 grid(unsigned((T + 127) / 128), unsigned((E + 127) / 128));
       hipLaunchKernelGGL(route_logits_kernel, grid, dim3(kThreads), 0, stream, x, planes, bias, logits, T, H, E);
