@@ -661,6 +661,138 @@ route_topk_vec_kernel(float* __restrict__ logits, const float* __restrict__ part
   }
 }
 
+// Reductions over one row of 16 lanes, the result in all 16: swap
+// neighbours, swap pairs, mirror the halves of 8, mirror the 16. Each step
+// combines a lane with its partner, and a partner's result with its own in
+// the other order, so (the operations being commutative) every lane of the
+// row ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ int row_peer(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, __int_as_float(row_peer<0xB1>(__float_as_int(v))));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, __int_as_float(row_peer<0x4E>(__float_as_int(v))));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, __int_as_float(row_peer<0x141>(__float_as_int(v))));  // row_half_mirror
+  v = fmaxf(v, __int_as_float(row_peer<0x140>(__float_as_int(v))));  // row_mirror
+  return v;
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += __int_as_float(row_peer<0xB1>(__float_as_int(v)));
+  v += __int_as_float(row_peer<0x4E>(__float_as_int(v)));
+  v += __int_as_float(row_peer<0x141>(__float_as_int(v)));
+  v += __int_as_float(row_peer<0x140>(__float_as_int(v)));
+  return v;
+}
+__device__ __forceinline__ uint32_t row_min16(uint32_t v) {
+  v = min(v, uint32_t(row_peer<0xB1>(int(v))));
+  v = min(v, uint32_t(row_peer<0x4E>(int(v))));
+  v = min(v, uint32_t(row_peer<0x141>(int(v))));
+  v = min(v, uint32_t(row_peer<0x140>(int(v))));
+  return v;
+}
+
+// Top-k for E = 16 Q experts (Q = 2, 4, 8, 16) and k <= 16, one row of 16
+// lanes per token, four tokens per wave: lane r of a row holds experts
+// Q r .. Q r + Q - 1. Same choices as route_topk_vec_kernel (part sums in
+// part order, then the bias; each round the largest live logit and, among
+// equal ones, the lowest expert id), with the wave-wide reductions replaced
+// by row-wide ones: a round is a row maximum of the lanes' live maxima, then
+// a row minimum of the ids that hold it. One token per wave leaves the vector
+// units doing a 64-lane reduction per selected expert; four per wave cut the
+// instructions per token about fourfold, and the kernel becomes bound by
+// its loads and stores. The softmax denominator over all E is a row sum
+// (summation order differs from the one-wave kernels, within float32
+// rounding); the renormalised one adds the k taken in order.
+template <int Q>
+__global__ void __launch_bounds__(kThreads)
+route_topk_row_kernel(float* __restrict__ logits, const float* __restrict__ part, int nparts,
+                      const float* __restrict__ bias, int T, int k, int renormalize, int32_t* __restrict__ topk_idx,
+                      float* __restrict__ topk_w) {
+  constexpr int E = 16 * Q;
+  const int lane = lane_id();
+  const int l16 = lane & 15;
+  const int t = int((int64_t(blockIdx.x) * kThreads + threadIdx.x) >> 4);
+  if (t >= T) return;  // whole rows: the row reductions below read only lanes of the same row
+  float* row = logits + int64_t(t) * E + Q * l16;
+  float v[Q];
+  load_q<Q>(row, v);
+  if (part != nullptr) {  // logits hold the first k part: add the others in order, then the bias; store the sum
+    const float* prow = part + int64_t(t) * E + Q * l16;
+    const int64_t pstride = int64_t(T) * E;
+    for (int z0 = 0; z0 < nparts; z0 += 4) {
+      float pv[4][Q];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (z0 + u < nparts) load_q<Q>(prow + (z0 + u) * pstride, pv[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (z0 + u < nparts)
+#pragma unroll
+          for (int i = 0; i < Q; ++i) v[i] += pv[u][i];
+    }
+    if (bias != nullptr) {
+      float b[Q];
+      if ((reinterpret_cast<uintptr_t>(bias) & 15u) == 0) {  // the same for every lane
+        load_q<Q>(bias + Q * l16, b);
+      } else {  // the bias may sit at any float address: one value per load
+#pragma unroll
+        for (int i = 0; i < Q; ++i) b[i] = bias[Q * l16 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < Q; ++i) v[i] += b[i];
+    }
+    store_q<Q>(row, v);
+  }
+  float lm = v[0];
+#pragma unroll
+  for (int i = 1; i < Q; ++i) lm = fmaxf(lm, v[i]);
+  const float m = row_max16(lm);
+
+  float den_all = 0.f;
+  if (!renormalize) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < Q; ++i) s += expf(v[i] - m);
+    den_all = row_sum16(s);
+  }
+
+  // A taken expert's value becomes NaN: the maximum ignores NaN and no NaN
+  // equals the row maximum, so it is never chosen again (a logit of -inf
+  // stays selectable).
+  const uint32_t base = uint32_t(Q * l16);
+  int my_e = 0;
+  float my_v = 0.f;
+  for (int j = 0; j < k; ++j) {
+    float cm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < Q; ++i) cm = fmaxf(cm, v[i]);
+    const float bv = row_max16(cm);
+    uint32_t cand = uint32_t(E);  // this lane's lowest expert holding the maximum
+#pragma unroll
+    for (int i = Q - 1; i >= 0; --i)
+      if (v[i] == bv) cand = base + uint32_t(i);
+    const uint32_t best = row_min16(cand);
+#pragma unroll
+    for (int i = 0; i < Q; ++i)
+      if (best == base + uint32_t(i)) v[i] = __int_as_float(0x7FC00000);
+    if (l16 == j) {
+      my_e = int(best);
+      my_v = bv;
+    }
+  }
+  const float p = l16 < k ? expf(my_v - m) : 0.f;
+  float den = den_all;
+  if (renormalize) {
+    den = 0.f;
+    for (int j = 0; j < k; ++j) den += shfl(p, (lane & ~15) + j);
+  }
+  if (l16 < k) {
+    topk_idx[int64_t(t) * k + l16] = my_e;
+    topk_w[int64_t(t) * k + l16] = p / den;
+  }
+}
+
 int route_k_parts(int T, int H, int E) {
   if (H % routedma::kSK != 0) return 1;
   const int nk_all = H / routedma::kSK;
@@ -719,6 +851,28 @@ hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b
   }
   {
     const float* pt = split ? part : nullptr;
+    // the vector loads and stores need 16-byte aligned rows (8-byte for two
+    // experts per lane; the partial sums live in the workspace, which is)
+    const uintptr_t la = reinterpret_cast<uintptr_t>(logits);
+    // (with few tokens the one-wave kernels spread the partial sums over
+    // more waves: a DeepSeek-R1-shaped decode step, T = 256 with 28 parts,
+    // routes in 24 us that way against 28 with rows)
+    if ((E == 32 || E == 64 || E == 128 || E == 256) && k <= 16 && T >= 2048 && (la & (E == 32 ? 7u : 15u)) == 0) {
+      dim3 rgrid(unsigned((int64_t(T) * 16 + kThreads - 1) / kThreads));
+#define MOE_TOPK_ROW(Q)                                                                                           \
+  hipLaunchKernelGGL(route_topk_row_kernel<Q>, rgrid, dim3(kThreads), 0, stream, logits, pt, parts - 1, bias, T, k, \
+                     renormalize, topk_idx, topk_w)
+      if (E == 32)
+        MOE_TOPK_ROW(2);
+      else if (E == 64)
+        MOE_TOPK_ROW(4);
+      else if (E == 128)
+        MOE_TOPK_ROW(8);
+      else
+        MOE_TOPK_ROW(16);
+#undef MOE_TOPK_ROW
+      return hipGetLastError();
+    }
     dim3 grid(unsigned((T + 3) / 4));
     const int epl = (E + 63) / 64;
 #define MOE_TOPK_VEC(Q)                                                                                          \

@@ -321,26 +321,36 @@ def test_pages_dispatch_examples(fixture):
             assert np.array_equal(yb[t], xf[t] if local else np.zeros(H))
 
 
-@pytest.mark.parametrize("E,k,renorm", [(4, 4, 1), (100, 7, 0), (256, 8, 1), (1000, 32, 1), (1024, 1, 0)])
-def test_topk_ties_and_edges(E, k, renorm):
+@pytest.mark.parametrize("E,k,renorm,T", [(4, 4, 1, 128), (100, 7, 0, 128), (256, 8, 1, 128), (1000, 32, 1, 128),
+                                          (1024, 1, 0, 128), (32, 4, 0, 2100), (64, 16, 1, 2048), (128, 5, 0, 2100),
+                                          (256, 16, 0, 2048), (256, 8, 1, 2099), (128, 8, 1, -2100)])
+def test_topk_ties_and_edges(E, k, renorm, T):
     """Selection with many exactly equal logits (ties go to the lowest expert
     id), signed zeros, experts pushed to -inf by the bias, E not a multiple of
     64 and the largest E and k. Logits are set exactly: token t's x is the
-    one-hot vector at position t, so logit[t, e] = w_router[e, t] + bias[e]."""
+    one-hot vector at position t % H, so logit[t, e] = w_router[e, t % H] +
+    bias[e]. E = 32, 64, 128, 256 with k <= 16 and T >= 2048 take the kernel
+    with one 16-lane row per token (T = 2099: the last wave holds three
+    tokens). A negative T means |T| tokens with the bias one float past a
+    16-byte boundary (element loads instead of vector loads)."""
     dev = device()
-    T = H = 128
-    rng = np.random.default_rng(E * 100 + k)
+    H = 128
+    bias_off = T < 0
+    T = abs(T)
+    rng = np.random.default_rng(E * 100 + k + 7 * T + bias_off)
     vals = np.array([-1.0, -0.0, 0.0, 0.5, 1.0, 2.0], np.float32)
-    wr = np.zeros((E, H), np.float32)
-    wr[:, :T] = vals[rng.integers(0, len(vals), size=(E, T))]
+    wr = vals[rng.integers(0, len(vals), size=(E, H))]
     bias = np.zeros(E, np.float32)
     bias[rng.choice(E, size=E // 4, replace=False)] = -np.inf
-    xf = np.eye(T, H, dtype=np.float32)
+    hot = np.arange(T) % H
+    xf = np.zeros((T, H), np.float32)
+    xf[np.arange(T), hot] = 1.0
     say(f"topk ties E={E} k={k} renorm={renorm}")
-    logits, idx, w = M.moe_route(to_dev_bf16(W.bf16_bits_from_f32(xf), dev), to_dev(wr, dev), to_dev(bias, dev), k,
+    bias_d = to_dev(np.concatenate([np.zeros(1, np.float32), bias]), dev)[1:] if bias_off else to_dev(bias, dev)
+    logits, idx, w = M.moe_route(to_dev_bf16(W.bf16_bits_from_f32(xf), dev), to_dev(wr, dev), bias_d, k,
                                  bool(renorm))
     lg = logits.cpu().numpy()
-    want_l = wr[:, :T].T.astype(np.float64) + bias[None, :]
+    want_l = wr[:, hot].T.astype(np.float64) + bias[None, :]
     assert np.array_equal(lg, want_l.astype(np.float32))
     want_idx = O.oracle_topk(lg, k)
     assert np.array_equal(idx.cpu().numpy(), want_idx)
