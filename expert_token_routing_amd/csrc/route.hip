@@ -262,7 +262,9 @@ route_logits_dma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
 // for bit. A stage is 32 KiB of token rows and 32 KiB of weight rows (256
 // bytes of one expert's row per stage; 16-byte chunk c of row r sits at
 // chunk position c ^ (r & 15), so the 16 rows a 16-lane read takes hit 16
-// different 16-byte slots).
+// different 16-byte slots). Every token tile repeats the cut (about 88 vector
+// instructions per 16-deep step per wave), so launch_route takes this kernel
+// only for a few token tiles, where dropping the plane pass pays.
 constexpr int kWStage = kBN * kSK * 4;                             // 32 KiB of float32 weight rows
 constexpr int kStageW = kAStage + kWStage;                         // 64 KiB
 
