@@ -9,10 +9,10 @@
 // [e0, e0 + E_local) ("Expert Parallelism (EP)", "Limitations").
 //
 // Row order is deterministic: segment of expert e0+i first by i, inside a
-// segment by token. Up to 1024 tokens, one workgroup builds every table in
-// one launch (dispatch_small_kernel); above that, four kernels (three when the
-// rows are copied: placement then happens in the copy kernel), no host
-// synchronisation:
+// segment by token. Up to 2048 tokens (1024 when the rows are copied too),
+// one workgroup builds every table in one launch (dispatch_small_kernel);
+// above that, four kernels (three when the rows are copied: placement then
+// happens in the copy kernel), no host synchronisation:
 //   1. histogram: one wave per chunk of 64 tokens counts its selections of
 //      every expert with LDS atomics -> chunk_table[e][chunk];
 //   2. scan: one workgroup per expert turns its row of chunk_table into
@@ -174,50 +174,49 @@ dispatch_index_kernel(const int32_t* __restrict__ topk_idx, const int32_t* __res
                    inv);
 }
 
-// Whole dispatch table build in one workgroup for T <= kSmallTokens: wave w
-// takes chunk w, and every lane ORs its bit into s_mask[w][e] for each of its
-// experts. Popcounts of those sets give each chunk's count of every expert
-// (counts, and the local segment starts by a scan), the selections of an
-// expert in earlier chunks, and the rank among earlier lanes of the chunk:
-// the rows are the multi-kernel path's, bit for bit. One launch instead of
-// three: for a decode step the three launches cost more than their work.
+// Whole dispatch table build in one workgroup, for T up to kSmallMaxTokens:
+// one launch instead of three (for few tokens the three launches cost more
+// than their work). First every selection is counted with LDS atomics
+// (counts, and the local segment starts by a scan). Then the tokens go by in
+// rounds of 16 chunks of 64, one chunk per wave: every lane ORs its bit into
+// s_mask[w][i] for each local expert i it picked, and a selection's row is
+// its segment start, plus the expert's selections in earlier rounds (s_run)
+// and in earlier chunks of this round, plus the earlier lanes of its chunk
+// that picked it (popcounts of those sets): the rows of the multi-kernel
+// path, bit for bit. Two rounds at most: the tables of `small_top2` (T =
+// 2048, top-2 of 8) take 10.5 us this way against 12.3 with three launches,
+// while the GPT-OSS-20B share (T = 8192, top-4 of 32; eight rounds) took 46
+// against 13.
 constexpr int kSmallWaves = 16;
-constexpr int kSmallTokens = kSmallWaves * kChunk;
+constexpr int kSmallTokens = kSmallWaves * kChunk;  // tokens per round
+constexpr int kSmallMaxTokens = 2 * kSmallTokens;
 
 template <int KMAX>
 __global__ void __launch_bounds__(kSmallWaves * 64)
 dispatch_small_kernel(const int32_t* __restrict__ topk_idx, int T, int E, int k, int e0, int E_local,
                       int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
                       int32_t* __restrict__ inv) {
-  __shared__ unsigned long long s_mask[kSmallWaves][1024];  // lanes of chunk w that picked expert e
+  __shared__ unsigned long long s_mask[kSmallWaves][1024];  // lanes of chunk w that picked local expert i
   __shared__ int s_cnt[1024];
   __shared__ int s_seg[1024 + 1];
+  __shared__ int s_run[1024];  // local expert i: its selections in earlier rounds
   __shared__ int s_tmp[kSmallWaves];
+  constexpr int kBlock = kSmallWaves * 64;
   const int wv = threadIdx.x >> 6;
   const int lane = lane_id();
-  const int t = wv * kChunk + lane;
-  const bool valid = t < T;
-  const int nw = int((T + kChunk - 1) / kChunk);  // chunks holding tokens
-  int ev[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) ev[j] = (j < k && valid) ? topk_idx[int64_t(t) * k + j] : -1;
-  for (int e = lane; e < E; e += 64) s_mask[wv][e] = 0ull;
+  for (int e = threadIdx.x; e < E; e += kBlock) s_cnt[e] = 0;
+  for (int i = threadIdx.x; i < E_local; i += kBlock) s_run[i] = 0;
   __syncthreads();
-  const unsigned long long bit = 1ull << lane;
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j)
-    if (j < k && valid) atomicOr(&s_mask[wv][ev[j]], bit);
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kSmallWaves * 64) {
-    int run = 0;
-    for (int w = 0; w < nw; ++w) run += __popcll(s_mask[w][e]);
-    counts[e] = run;
-    if (e >= e0 && e < e0 + E_local) s_cnt[e - e0] = run;
+  const int64_t nsel = int64_t(T) * k;
+  for (int64_t s = threadIdx.x; s < nsel; s += kBlock) {
+    const int e = topk_idx[s];
+    if (unsigned(e) < unsigned(E)) atomicAdd(&s_cnt[e], 1);
   }
   __syncthreads();
-  const int c = int(threadIdx.x) < E_local ? s_cnt[threadIdx.x] : 0;
+  for (int e = threadIdx.x; e < E; e += kBlock) counts[e] = s_cnt[e];
+  const int c = int(threadIdx.x) < E_local ? s_cnt[e0 + threadIdx.x] : 0;
   int tot;
-  const int pre = block_exclusive_scan<kSmallWaves * 64>(c, s_tmp, tot);
+  const int pre = block_exclusive_scan<kBlock>(c, s_tmp, tot);
   if (int(threadIdx.x) < E_local) {
     s_seg[threadIdx.x] = pre;
     offsets[threadIdx.x] = pre;
@@ -226,23 +225,44 @@ dispatch_small_kernel(const int32_t* __restrict__ topk_idx, int T, int E, int k,
     s_seg[E_local] = tot;
     offsets[E_local] = tot;
   }
-  __syncthreads();
-  if (!valid) return;
   const uint64_t lt = lanemask_lt();
+  const unsigned long long bit = 1ull << lane;
+  for (int r0 = 0; r0 < T; r0 += kSmallTokens) {
+    const int t = r0 + wv * kChunk + lane;
+    const bool valid = t < T;
+    // (this wave's row only: its own LDS operations stay in order)
+    for (int i = lane; i < E_local; i += 64) s_mask[wv][i] = 0ull;
+    int ev[KMAX];
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    if (j < k) {
-      const int e = ev[j];
-      const int64_t slot = int64_t(t) * k + j;
-      if (e >= e0 && e < e0 + E_local) {
-        int row = s_seg[e - e0] + __popcll(s_mask[wv][e] & lt);
-        for (int w = 0; w < wv; ++w) row += __popcll(s_mask[w][e]);
-        perm_src[row] = int32_t(slot);
-        inv[slot] = row;
-      } else {
-        inv[slot] = -1;
+    for (int j = 0; j < KMAX; ++j) ev[j] = (j < k && valid) ? topk_idx[int64_t(t) * k + j] - e0 : -1;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (j < k && valid && unsigned(ev[j]) < unsigned(E_local)) atomicOr(&s_mask[wv][ev[j]], bit);
+    __syncthreads();  // every chunk's sets complete; s_seg and s_run written
+    if (valid) {
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (j < k) {
+          const int i = ev[j];
+          const int64_t slot = int64_t(t) * k + j;
+          if (unsigned(i) < unsigned(E_local)) {
+            int row = s_seg[i] + s_run[i] + __popcll(s_mask[wv][i] & lt);
+            for (int w = 0; w < wv; ++w) row += __popcll(s_mask[w][i]);
+            perm_src[row] = int32_t(slot);
+            inv[slot] = row;
+          } else {
+            inv[slot] = -1;
+          }
+        }
       }
     }
+    __syncthreads();  // every placement read s_run and the sets
+    for (int i = threadIdx.x; i < E_local; i += kBlock) {
+      int add = 0;
+      for (int w = 0; w < kSmallWaves; ++w) add += __popcll(s_mask[w][i]);
+      s_run[i] += add;
+    }
+    __syncthreads();  // s_run updated before the next round's placements; sets free
   }
 }
 
@@ -373,7 +393,7 @@ size_t dispatch_table_bytes(int T, int E) {
 hipError_t launch_dispatch_index(const int32_t* topk_idx, int T, int E, int k, int e0, int E_local, int32_t* counts,
                                  int32_t* offsets, int32_t* perm_src, int32_t* inv, int32_t* chunk_table,
                                  hipStream_t stream) {
-  if (T <= kSmallTokens) {
+  if (T <= kSmallMaxTokens) {
 #define MOE_SMALL_LAUNCH(KM)                                                                                  \
   hipLaunchKernelGGL(dispatch_small_kernel<KM>, dim3(1), dim3(kSmallWaves * 64), 0, stream, topk_idx, T, E, k, \
                      e0, E_local, counts, offsets, perm_src, inv)

@@ -421,6 +421,36 @@ def test_deterministic_and_row_independent():
     assert torch.equal(yp.view(torch.int16), y1[p].view(torch.int16))
 
 
+@pytest.mark.parametrize("T,E,k,e0,E_local", [(700, 40, 4, 8, 8), (1100, 24, 5, 4, 12), (2048, 8, 2, 0, 8),
+                                               (2049, 16, 3, 2, 9)])
+def test_forward_tables_match_oracle(T, E, k, e0, E_local):
+    """The dispatch tables moe_forward builds in its workspace (one workgroup
+    in one or two rounds of 1024 tokens up to T = 2048, three kernels above)
+    equal the oracle's stable permutation on the forward's own top-k ids."""
+    dev = device()
+    cfg = W.MoEConfig(f"tables{T}", T=T, H=64, I=64, E=E, k=k, e0=e0, E_local=E_local)
+    d = DevInputs(W.make_inputs(cfg), dev)
+    ws = torch.empty(M.forward_workspace_size(T, cfg.H, cfg.I, E, k, E_local), dtype=torch.uint8, device=dev)
+    say(f"moe_forward tables T={T} E={E} k={k} e0={e0} E_local={E_local}")
+    M.moe_forward(d.x, d.w_router, d.bias, d.w_gate_up, d.w_down, k, e0, cfg.renormalize, workspace=ws)
+    torch.cuda.synchronize()
+    lay = M.forward_workspace_layout(T, cfg.H, cfg.I, E, k, E_local)
+    host = ws.cpu().numpy()
+
+    def i32(name, n):
+        return host[lay[name]:lay[name] + 4 * n].view(np.int32)
+
+    idx = i32("topk_idx", T * k).reshape(T, k)
+    rc = O.oracle_counts(idx, E)
+    ro = O.oracle_offsets(rc, e0, E_local)
+    rp, rinv = O.oracle_permutation(idx, e0, E_local)
+    assert np.array_equal(i32("counts", E), rc)
+    assert np.array_equal(i32("offsets", E_local + 1), ro)
+    N = int(ro[-1])
+    assert np.array_equal(i32("perm_src", N), rp)
+    assert np.array_equal(i32("inv", T * k), rinv)
+
+
 def test_empty_batch_is_noop():
     dev = device()
     cfg = W.MoEConfig("empty", T=0, H=64, I=64, E=4, k=2, e0=0, E_local=4)
