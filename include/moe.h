@@ -226,7 +226,8 @@ int moe_forward(const moe_bf16* x, const float* w_router, const float* bias,
  *   - MOE_ERR_WORKSPACE (nothing launched) when the problem needs more than
  *     the array holds, i.e. moe_forward_workspace_size(T, H, I, E, k,
  *     E_local) > MOE_NOALLOC_SCRATCH_BYTES (a DeepSeek-R1-shaped EP=8 rank
- *     share needs about 56 MB at T = 256 tokens, 192 MB at T = 1024).
+ *     share needs about 54 MB at T = 256 tokens, 183 MB at T = 1024; the
+ *     limit admits up to T = 698).
  *   - the array is shared by every call on one GPU and keeps the last call's
  *     contents; no part of it needs to start at zero. Calls that overlap on
  *     one GPU (two streams, two threads) race on it and must be ordered by
