@@ -315,39 +315,53 @@ __device__ __forceinline__ void split3(const u32x4& c0, const u32x4& c1, u32x4& 
   }
 }
 
+// BM tokens x kBN experts per workgroup: 256 tokens as 4 x 2 waves of 64 x 64
+// (2 x 2 fragments of 32 x 32), or 64 tokens as 2 x 4 waves of 32 x 32 (one
+// fragment), for few tokens, where four times the workgroups keep four times
+// the CUs busy.
+template <int BM>
 __global__ void __launch_bounds__(dma::kThreads)
 route_logits_w32_kernel(const uint16_t* __restrict__ x, const float* __restrict__ w_router, float* __restrict__ out0,
                         float* __restrict__ out1, int T, int H, int E, int per) {
   using namespace dma;
-  __shared__ __attribute__((aligned(1024))) char smem[kBufs * kStageW];
+  static_assert(BM == 256 || BM == 64, "tile heights");
+  constexpr int kWM = BM == 256 ? 4 : 2;  // wave rows
+  constexpr int kWN = kWaves / kWM;       // wave columns
+  constexpr int kRM = BM / kWM;           // tokens per wave
+  constexpr int kCN = kBN / kWN;          // experts per wave
+  constexpr int FM = kRM / 32, FN = kCN / 32;
+  constexpr int kAStg = BM * kSK * 2;
+  constexpr int kStg = kAStg + kWStage;
+  __shared__ __attribute__((aligned(1024))) char smem[kBufs * kStg];
   MOE_LDS char* lds = (MOE_LDS char*)smem;
-  const int t0 = blockIdx.x * kBM;
+  const int t0 = blockIdx.x * BM;
   const int n0 = blockIdx.y * kBN;
-  const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int w = threadIdx.x >> 6, wm = w / kWN, wn = w % kWN;
   const int lane = lane_id();
   const int nk_all = H / kSK;
   const int s0 = blockIdx.z * per;
   const int nk = max(0, min(nk_all, s0 + per) - s0);  // stages of this part
   float* __restrict__ out = blockIdx.z == 0 ? out0 : out1 + int64_t(blockIdx.z - 1) * T * E;
 
-  RowLoader64<kBM> la;
+  RowLoader64<BM> la;
   RowLoaderF32<kBN> lb;
-  la.init(x + int64_t(t0) * H, H, min(kBM, T - t0));
+  la.init(x + int64_t(t0) * H, H, min(BM, T - t0));
   lb.init(w_router + int64_t(n0) * H, H, min(kBN, E - n0));
   auto issue = [&](int st) {
     if (st < nk) {
-      MOE_LDS char* dst = lds + (st % kBufs) * kStageW;
+      MOE_LDS char* dst = lds + (st % kBufs) * kStg;
       la.issue(dst, (s0 + st) * kSK);
-      lb.issue(dst + kAStage, (s0 + st) * kSK);
+      lb.issue(dst + kAStg, (s0 + st) * kSK);
     }
   };
-  // fragment offsets of 16-deep step ks (0..3): A rows wm*64 + fm*32 + lane%32,
-  // chunk 2 ks + lane/32 (swizzled as RowLoader64); weight rows wn*64 +
-  // fn*32 + lane%32, float32 chunks 4 ks + 2 (lane/32) and +1 (swizzled as
-  // RowLoaderF32; the row bits the swizzle uses are those of lane%32)
+  // fragment offsets of 16-deep step ks (0..3): A rows wm*kRM + fm*32 +
+  // lane%32, chunk 2 ks + lane/32 (swizzled as RowLoader64); weight rows
+  // wn*kCN + fn*32 + lane%32, float32 chunks 4 ks + 2 (lane/32) and +1
+  // (swizzled as RowLoaderF32; the row bits the swizzle uses are those of
+  // lane%32)
   const int khalf = lane >> 5;
-  const int ma = wm * 64 + (lane & 31);
-  const int mb = wn * 64 + (lane & 31);
+  const int ma = wm * kRM + (lane & 31);
+  const int mb = wn * kCN + (lane & 31);
   uint32_t aoff[kSK / 16], woff[kSK / 16][2];
 #pragma unroll
   for (int ks = 0; ks < kSK / 16; ++ks) {
@@ -356,38 +370,38 @@ route_logits_w32_kernel(const uint16_t* __restrict__ x, const float* __restrict_
     for (int e = 0; e < 2; ++e) woff[ks][e] = uint32_t(mb * 256 + 16 * ((4 * ks + 2 * khalf + e) ^ (mb & 15)));
   }
   struct F {
-    u32x4 a[kFM];
-    u32x4 wv[kFN][2];
+    u32x4 a[FM];
+    u32x4 wv[FN][2];
   };
   auto load = [&](const MOE_LDS char* st, int ks, F& f) {
 #pragma unroll
-    for (int fm = 0; fm < kFM; ++fm)
+    for (int fm = 0; fm < FM; ++fm)
       f.a[fm] = *reinterpret_cast<const MOE_LDS u32x4*>(st + aoff[ks] + fm * 32 * 128);
 #pragma unroll
-    for (int fn = 0; fn < kFN; ++fn)
+    for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
       for (int e = 0; e < 2; ++e)
-        f.wv[fn][e] = *reinterpret_cast<const MOE_LDS u32x4*>(st + kAStage + woff[ks][e] + fn * 32 * 256);
+        f.wv[fn][e] = *reinterpret_cast<const MOE_LDS u32x4*>(st + kAStg + woff[ks][e] + fn * 32 * 256);
   };
-  f32x16 acc[kFM][kFN];
+  f32x16 acc[FM][FN];
 #pragma unroll
-  for (int fm = 0; fm < kFM; ++fm)
+  for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-    for (int fn = 0; fn < kFN; ++fn)
+    for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[fm][fn][v] = 0.f;
   auto mma = [&](const F& f) {
-    u32x4 b[kPlanes][kFN];
+    u32x4 b[kPlanes][FN];
 #pragma unroll
-    for (int fn = 0; fn < kFN; ++fn) split3(f.wv[fn][0], f.wv[fn][1], b[0][fn], b[1][fn], b[2][fn]);
+    for (int fn = 0; fn < FN; ++fn) split3(f.wv[fn][0], f.wv[fn][1], b[0][fn], b[1][fn], b[2][fn]);
 #pragma unroll
     for (int p = 0; p < kPlanes; ++p)
 #pragma unroll
-      for (int fm = 0; fm < kFM; ++fm)
+      for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < kFN; ++fn) acc[fm][fn] = mfma32x32x16(f.a[fm], b[p][fn], acc[fm][fn]);
+        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma32x32x16(f.a[fm], b[p][fn], acc[fm][fn]);
   };
-  constexpr int kLoads = RowLoader64<kBM>::kPer + RowLoaderF32<kBN>::kPer;  // DMA instructions per wave per stage
+  constexpr int kLoads = RowLoader64<BM>::kPer + RowLoaderF32<kBN>::kPer;  // DMA instructions per wave per stage
 
   if (nk > 0) {
     issue(0);
@@ -399,7 +413,7 @@ route_logits_w32_kernel(const uint16_t* __restrict__ x, const float* __restrict_
     F f0, f1;
     load(lds, 0, f0);
     for (int kt = 0; kt < nk; ++kt) {
-      const MOE_LDS char* cur = lds + (kt % kBufs) * kStageW;
+      const MOE_LDS char* cur = lds + (kt % kBufs) * kStg;
       // steps 0..2: each step's MFMAs cover the next step's LDS reads
       load(cur, 1, f1);
       mma(f0);
@@ -415,7 +429,7 @@ route_logits_w32_kernel(const uint16_t* __restrict__ x, const float* __restrict_
       wait_lgkm0();
       wait_vm_barrier<0>();
       issue(kt + 2);
-      load(lds + ((kt + 1) % kBufs) * kStageW, 0, f0);  // stage nk: a finished buffer, values unused
+      load(lds + ((kt + 1) % kBufs) * kStg, 0, f0);  // stage nk: a finished buffer, values unused
       mma(f1);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -423,13 +437,13 @@ route_logits_w32_kernel(const uint16_t* __restrict__ x, const float* __restrict_
   }
 
 #pragma unroll
-  for (int fn = 0; fn < kFN; ++fn) {
+  for (int fn = 0; fn < FN; ++fn) {
     const int e = n0 + mb + fn * 32;
 #pragma unroll
-    for (int fm = 0; fm < kFM; ++fm)
+    for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int t = t0 + wm * 64 + fm * 32 + mfma_c_row(v, lane);
+        const int t = t0 + wm * kRM + fm * 32 + mfma_c_row(v, lane);
         if (t < T && e < E) out[int64_t(t) * E + e] = acc[fm][fn][v];
       }
   }
@@ -838,8 +852,11 @@ hipError_t launch_route(const uint16_t* x, const float* w_router, const float* b
       const int per = (nk_all + parts - 1) / parts;
       dim3 grid(unsigned((T + routedma::kBM - 1) / routedma::kBM), unsigned((E + routedma::kBN - 1) / routedma::kBN),
                 unsigned(parts));
-      if (w32)
-        hipLaunchKernelGGL(routedma::route_logits_w32_kernel, grid, dim3(dma::kThreads), 0, stream, x, w_router,
+      if (w32 && T <= 512)  // decode-sized batches: 64-token tiles, four times the workgroups
+        hipLaunchKernelGGL(routedma::route_logits_w32_kernel<64>, dim3(unsigned((T + 63) / 64), grid.y, grid.z),
+                           dim3(dma::kThreads), 0, stream, x, w_router, logits, part, T, H, E, per);
+      else if (w32)
+        hipLaunchKernelGGL(routedma::route_logits_w32_kernel<256>, grid, dim3(dma::kThreads), 0, stream, x, w_router,
                            logits, part, T, H, E, per);
       else
         hipLaunchKernelGGL(routedma::route_logits_dma_kernel, grid, dim3(dma::kThreads), 0, stream, x, planes, logits,

@@ -228,13 +228,15 @@ def check_combine(cfg, res, gw, rinv):
 # --------------------------------------------------------------------------- #
 # tests                                                                        #
 # --------------------------------------------------------------------------- #
-@pytest.mark.parametrize("T,H,E", [(192, 136, 70), (192, 1216, 70), (100, 7168, 256), (2500, 1216, 70)])
+@pytest.mark.parametrize("T,H,E", [(192, 136, 70), (192, 1216, 70), (100, 7168, 256), (1000, 1216, 70),
+                                   (2500, 1216, 70)])
 def test_mfma_router_split_is_exact(T, H, E):
     """One-hot tokens make each logit a single product x*w = w, so the three
     bf16 parts must add back to the float32 router weight exactly (and every
     other k part of a split sum adds zeros). The k-split cases cover both
-    cuts: in registers for a few token tiles (T <= 2048), through the plane
-    pass beyond (T = 2500: 10 tiles of 256 tokens, 4 parts)."""
+    cuts: in registers for a few token tiles (T <= 2048; 64-token tiles up to
+    T = 512, 256-token tiles at T = 1000), through the plane pass beyond
+    (T = 2500: 10 tiles of 256 tokens, 4 parts)."""
     dev = device()
     rng = np.random.default_rng(5)
     xf = np.zeros((T, H), np.float32)
