@@ -613,14 +613,17 @@ route_topk_vec_kernel(float* __restrict__ logits, const float* __restrict__ part
   if (part != nullptr) {  // logits hold the first k part: add the others in order, then the bias; store the sum
     const float* prow = part + int64_t(t) * E + Q * lane;
     const int64_t pstride = int64_t(T) * E;
-    // four parts' loads in flight at a time, added in part order
-    for (int z0 = 0; z0 < nparts; z0 += 4) {
-      float pv[4][Q];
+    // U parts' loads in flight at a time (64 values a lane), added in part
+    // order (a decode step with 28 parts: 19.7 -> 18.8 us for the route
+    // stage against four at a time)
+    constexpr int U = 64 / Q < 4 ? 4 : (64 / Q > 16 ? 16 : 64 / Q);
+    for (int z0 = 0; z0 < nparts; z0 += U) {
+      float pv[U][Q];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < U; ++u)
         if (z0 + u < nparts) load_q<Q>(prow + (z0 + u) * pstride, pv[u]);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < U; ++u)
         if (z0 + u < nparts)
 #pragma unroll
           for (int i = 0; i < Q; ++i) v[i] += pv[u][i];
